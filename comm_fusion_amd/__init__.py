@@ -1,0 +1,21 @@
+"""MI355X (gfx950) Ulysses-shard attention with the post-attention All-to-All
+fused into the output epilogue.
+
+Thin ctypes binding over ``libulysses_attn.so`` (C ABI in
+``include/ulysses_attn.h``).  It only marshals arguments: tensor pointers,
+shapes and the current HIP stream.  Every step of the computation runs in the
+library's HIP kernels; if the library is not built this package raises instead
+of computing anything itself.
+
+Names and arguments follow the C calls:
+  attn_ulysses_fused(Q, K, V, rank, P, out, scale=None, stream=None)
+  attn_serial(Q, K, V, rank, P, O_local, scale=None, stream=None)
+  a2a_permute(O_local, rank, P, out, stream=None)
+Tensors are torch tensors on the GPU: Q, K, V, O_local bfloat16
+[B][S][Hl][d]; out bfloat16 with B*S*(Hl*P)*d elements, laid out
+[B][P][S/P][H][d].
+"""
+from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # noqa: F401
+                       UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_OK, UAError, a2a_permute,
+                       attn_serial, attn_ulysses_fused, dest_bytes, lib, lib_path,
+                       local_bytes, status_string, version)

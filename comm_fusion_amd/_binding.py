@@ -1,0 +1,148 @@
+"""ctypes marshalling for libulysses_attn.so (see include/ulysses_attn.h)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libulysses_attn.so")
+
+UA_OK = 0
+UA_ERR_NULL = -1
+UA_ERR_SHAPE = -2
+UA_ERR_RANK = -3
+UA_ERR_ALIGN = -4
+UA_ERR_UNSUPPORTED = -5
+UA_ERR_HIP = -6
+
+
+class UAError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (call, status_string(status), status))
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("S", ctypes.c_int64),
+                ("H", ctypes.c_int64), ("d", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libulysses_attn.so is not built (%s); run "
+                          "`python -m comm_fusion_amd.build` or __graft_entry__.build()" % _LIB_PATH)
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sp = ctypes.POINTER(Shape)
+    L.attn_ulysses_fused.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
+    L.attn_ulysses_fused.restype = i
+    L.attn_serial.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
+    L.attn_serial.restype = i
+    L.a2a_permute.argtypes = [vp, i, i, vp, sp, vp]
+    L.a2a_permute.restype = i
+    L.ua_status_string.argtypes = [i]
+    L.ua_status_string.restype = ctypes.c_char_p
+    L.ua_dest_bytes.argtypes = [sp]
+    L.ua_dest_bytes.restype = ctypes.c_size_t
+    L.ua_local_bytes.argtypes = [sp, i]
+    L.ua_local_bytes.restype = ctypes.c_size_t
+    L.ua_version.argtypes = []
+    L.ua_version.restype = i
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().ua_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().ua_version())
+
+
+def dest_bytes(B, S, H, d) -> int:
+    return int(lib().ua_dest_bytes(ctypes.byref(Shape(B, S, H, d))))
+
+
+def local_bytes(B, S, H, d, P) -> int:
+    return int(lib().ua_local_bytes(ctypes.byref(Shape(B, S, H, d)), int(P)))
+
+
+def _ptr(t) -> int:
+    return int(t.data_ptr()) if t is not None else 0
+
+
+def _check_bf16(name, t, numel=None):
+    import torch
+    if t is None:
+        return
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous bfloat16 GPU tensor" % name)
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _qkv_shape(Q, K, V, P):
+    if Q.dim() != 4 or tuple(K.shape) != tuple(Q.shape) or tuple(V.shape) != tuple(Q.shape):
+        raise ValueError("Q, K, V must share one [B][S][Hl][d] shape")
+    B, S, Hl, d = (int(x) for x in Q.shape)
+    return Shape(B, S, Hl * int(P), d)
+
+
+def attn_ulysses_fused(Q, K, V, rank, P, out, scale=None, stream=None):
+    """Fused attention + post-attention All-to-All into ``out`` [B][P][S/P][H][d]."""
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_ulysses_fused(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
+                                  ctypes.byref(shp), scale, _stream(stream))
+    if st != UA_OK:
+        raise UAError("attn_ulysses_fused", st)
+
+
+def attn_serial(Q, K, V, rank, P, O_local, scale=None, stream=None):
+    """Attention only, into the head-partitioned ``O_local`` [B][S][Hl][d]."""
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("O_local", O_local, Q.numel())
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_serial(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(O_local),
+                           ctypes.byref(shp), scale, _stream(stream))
+    if st != UA_OK:
+        raise UAError("attn_serial", st)
+
+
+def a2a_permute(O_local, rank, P, out, stream=None):
+    """Serial All-to-All: copy ``O_local`` rows into their slots of ``out``."""
+    if O_local.dim() != 4:
+        raise ValueError("O_local must be [B][S][Hl][d]")
+    B, S, Hl, d = (int(x) for x in O_local.shape)
+    shp = Shape(B, S, Hl * int(P), d)
+    _check_bf16("O_local", O_local)
+    _check_bf16("out", out, B * S * Hl * int(P) * d)
+    st = lib().a2a_permute(_ptr(O_local), int(rank), int(P), _ptr(out), ctypes.byref(shp),
+                           _stream(stream))
+    if st != UA_OK:
+        raise UAError("a2a_permute", st)

@@ -1,0 +1,167 @@
+// ua_api.cpp -- C ABI of libulysses_attn.so (declared in include/ulysses_attn.h).
+//
+// Host-side only: argument validation (no device access, so it runs on a
+// host without a GPU), placement set-up for the two epilogues, and launches.
+// The library allocates nothing and keeps no state between calls.
+
+#include "ulysses_attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "ua_internal.h"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape-level checks shared by every entry point.  On success *elems holds
+// B*S*H*d (the destination element count).
+int check_shape(const ua_shape *shp, int rank, int P, int64_t *elems)
+{
+    if (!shp) return UA_ERR_NULL;
+    const int64_t B = shp->B, S = shp->S, H = shp->H, d = shp->d;
+    if (B < 0 || S < 0 || H < 1 || d < 1 || P < 1) return UA_ERR_SHAPE;
+    if (H % P != 0 || S % P != 0) return UA_ERR_SHAPE;
+    int64_t n = 0;
+    if (!mul_ok(B, S, &n) || !mul_ok(n, H, &n) || !mul_ok(n, d, &n) || n > INT64_MAX / 2)
+        return UA_ERR_SHAPE;
+    if (rank < 0 || rank >= P) return UA_ERR_RANK;
+    if (d != 64 && d != 128) return UA_ERR_UNSUPPORTED;
+    *elems = n;
+    return UA_OK;
+}
+
+// Size limits of the launch grids: work units and copied 16-byte chunks are
+// counted in 32-bit integers.
+int check_limits(const ua_shape *shp, int P)
+{
+    const int64_t Hl = shp->H / P;
+    const int64_t rows = shp->B * shp->S * Hl;
+    if (rows >= (int64_t)1 << 31) return UA_ERR_UNSUPPORTED;
+    if (rows * (shp->d / 8) > (int64_t)UINT32_MAX) return UA_ERR_UNSUPPORTED;
+    if (ua::attention_units(shp->B, shp->S, Hl) > INT32_MAX) return UA_ERR_UNSUPPORTED;
+    return UA_OK;
+}
+
+bool empty(const ua_shape *shp) { return shp->B == 0 || shp->S == 0; }
+
+ua::Placement dest_placement(void *out, const ua_shape *shp, int rank, int P)
+{
+    ua::Placement o;
+    o.base = (uint16_t *)out;
+    o.regions = P;
+    o.region_rows = shp->S / P;
+    o.heads = shp->H;
+    o.head0 = (int64_t)rank * (shp->H / P);
+    return o;
+}
+
+ua::Placement local_placement(void *o_local, const ua_shape *shp, int P)
+{
+    ua::Placement o;
+    o.base = (uint16_t *)o_local;
+    o.regions = 1;
+    o.region_rows = shp->S;
+    o.heads = shp->H / P;
+    o.head0 = 0;
+    return o;
+}
+
+int attention_call(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                   const ua_shape *shp, float scale, void *stream, bool fused)
+{
+    int64_t elems = 0;
+    int st = check_shape(shp, rank, P, &elems);
+    if (st != UA_OK) return st;
+    if (!isfinite(scale) || !(scale > 0.0f)) return UA_ERR_UNSUPPORTED;
+    if ((st = check_limits(shp, P)) != UA_OK) return st;
+    if (empty(shp)) return UA_OK;
+    if (!Q || !K || !V || !out) return UA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return UA_ERR_ALIGN;
+    const ua::Placement o = fused ? dest_placement(out, shp, rank, P) : local_placement(out, shp, P);
+    const hipError_t e = ua::launch_attention((const uint16_t *)Q, (const uint16_t *)K,
+                                              (const uint16_t *)V, shp->B, shp->S, shp->H / P,
+                                              (int)shp->d, scale, o, (hipStream_t)stream);
+    return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_ulysses_fused(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                       const ua_shape *shp, float scale, void *stream)
+{
+    return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true);
+}
+
+int attn_serial(const void *Q, const void *K, const void *V, int rank, int P, void *O_local,
+                const ua_shape *shp, float scale, void *stream)
+{
+    return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false);
+}
+
+int a2a_permute(const void *O_local, int rank, int P, void *out, const ua_shape *shp, void *stream)
+{
+    int64_t elems = 0;
+    int st = check_shape(shp, rank, P, &elems);
+    if (st != UA_OK) return st;
+    if ((st = check_limits(shp, P)) != UA_OK) return st;
+    if (empty(shp)) return UA_OK;
+    if (!O_local || !out) return UA_ERR_NULL;
+    if (!aligned16(O_local) || !aligned16(out)) return UA_ERR_ALIGN;
+    const hipError_t e = ua::launch_permute((const uint16_t *)O_local, shp->B, shp->S, shp->H / P,
+                                            (int)shp->d, dest_placement(out, shp, rank, P),
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+const char *ua_status_string(int status)
+{
+    switch (status) {
+    case UA_OK: return "ok";
+    case UA_ERR_NULL: return "a required pointer is NULL";
+    case UA_ERR_SHAPE: return "invalid shape (negative dims, H or P < 1, S or H not divisible by P, or size overflow)";
+    case UA_ERR_RANK: return "rank outside [0, P)";
+    case UA_ERR_ALIGN: return "a buffer pointer is not 16-byte aligned";
+    case UA_ERR_UNSUPPORTED: return "unsupported (d not 64/128, scale not finite and > 0, or shape beyond launch limits)";
+    case UA_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+    }
+}
+
+size_t ua_dest_bytes(const ua_shape *shp)
+{
+    if (!shp || shp->B < 0 || shp->S < 0 || shp->H < 1 || shp->d < 1) return 0;
+    int64_t e = 0;
+    if (!mul_ok(shp->B, shp->S, &e) || !mul_ok(e, shp->H, &e) || !mul_ok(e, shp->d, &e) ||
+        e > INT64_MAX / 2)
+        return 0;
+    return (size_t)e * 2;
+}
+
+size_t ua_local_bytes(const ua_shape *shp, int P)
+{
+    if (!shp || P < 1 || shp->B < 0 || shp->S < 0 || shp->H < 1 || shp->d < 1 || shp->H % P != 0)
+        return 0;
+    int64_t e = 0;
+    if (!mul_ok(shp->B, shp->S, &e) || !mul_ok(e, shp->H / P, &e) || !mul_ok(e, shp->d, &e) ||
+        e > INT64_MAX / 2)
+        return 0;
+    return (size_t)e * 2;
+}
+
+int ua_version(void) { return kVersion; }
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// ua_internal.h -- launch interface between the C-ABI layer (ua_api.cpp) and
+// the gfx950 kernels (ua_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ua {
+
+// Where attention output rows go.  One description serves both epilogues:
+//   destination [B][P][S/P][H][d]: regions = P, region_rows = S/P,
+//                                  heads = H, head0 = rank*Hl;
+//   local       [B][S][Hl][d]:     regions = 1, region_rows = S,
+//                                  heads = Hl, head0 = 0.
+// Row s of local head h of batch b goes to region p = s / region_rows, row
+// i = s - p*region_rows, head g = head0 + h, i.e. element offset
+// (((b*regions + p)*region_rows + i)*heads + g)*d.
+struct Placement {
+    uint16_t *base;
+    int64_t regions;
+    int64_t region_rows;
+    int64_t heads;
+    int64_t head0;
+};
+
+// Attention over Hl local heads of [B][S][Hl][d] Q, K, V (bf16 bits).
+hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            int64_t B, int64_t S, int64_t Hl, int d, float scale,
+                            const Placement &out, hipStream_t stream);
+
+// Bit copy of O_local [B][S][Hl][d] rows into `out`.
+hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t Hl, int d,
+                          const Placement &out, hipStream_t stream);
+
+// Work units (one workgroup each) the attention launch uses for this shape.
+int64_t attention_units(int64_t B, int64_t S, int64_t Hl);
+
+}  // namespace ua

@@ -1,0 +1,112 @@
+/*
+ * ulysses_attn.h -- C ABI of the MI355X (gfx950) Ulysses-shard attention
+ * library, libulysses_attn.so.
+ *
+ * The operation (X-Stage paper, arXiv 2607.23264):
+ *   Fig. 5 of the pith.science review page, steps (a)-(c): after the
+ *   pre-attention All-to-All, rank r of a P-rank Ulysses group holds the full
+ *   sequence S for Hl = H/P heads.  Steps (d)-(e): attention runs on those
+ *   heads and the post-attention All-to-All sends each output row back to the
+ *   rank that owns its sequence chunk.  The abstract describes the fused form:
+ *   the owner of an output tile stores it straight into the destination slot
+ *   and resumes computing, with no wavefront or CU set aside for the exchange.
+ *
+ * Attention is non-causal softmax(Q K^T * scale) V per head, no mask, no
+ * dropout, computed with bf16 inputs, fp32 accumulation and bf16 output
+ * (round to nearest even).
+ *
+ * Layouts (bf16 = IEEE binary16-brain, passed as raw 16-bit patterns):
+ *   Q, K, V, O_local : [B][S][Hl][d], contiguous, Hl = H / P.
+ *   out (destination): [B][P][S/P][H][d], contiguous: P back-to-back regions,
+ *       region p holding sequence rows [p*S/P, (p+1)*S/P) of all H heads.
+ *       Row s of local head h_l lands in region p = s / (S/P), local row
+ *       i = s mod (S/P), global head g = rank*Hl + h_l.
+ *       (Because the regions are adjacent, this buffer is byte-identical to a
+ *       [B][S][H][d] tensor: running every rank fills the full output.)
+ *
+ * Ownership: the caller allocates and frees every buffer; the library
+ * allocates nothing and keeps no state between calls.  A call writes only
+ * this rank's Hl head slots of `out` (every other slot keeps its bytes).
+ * Output buffers must not overlap the inputs.
+ *
+ * Pointers Q, K, V, out, O_local are DEVICE pointers on the current HIP
+ * device, 16-byte aligned.  `stream` is a hipStream_t (NULL = default
+ * stream).  Calls are asynchronous: they return after the launch.
+ *
+ * Errors: every call returns a status code and never prints or aborts.
+ * Arguments are validated on the host before any device access, in this
+ * order: null pointers, shape, rank, alignment, support; a launch failure
+ * reported by the runtime gives UA_ERR_HIP.
+ */
+#ifndef ULYSSES_ATTN_H
+#define ULYSSES_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int64_t B; /* batch                                    (>= 0)          */
+    int64_t S; /* full sequence length                     (>= 0, S % P == 0) */
+    int64_t H; /* total heads of the Ulysses group         (>= 1, H % P == 0) */
+    int64_t d; /* head dimension                           (64 or 128)     */
+} ua_shape;
+
+enum {
+    UA_OK = 0,
+    UA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+    UA_ERR_SHAPE = -2,       /* negative dims, H < 1, P < 1, S % P, H % P, overflow */
+    UA_ERR_RANK = -3,        /* rank outside [0, P)                            */
+    UA_ERR_ALIGN = -4,       /* a buffer pointer is not 16-byte aligned        */
+    UA_ERR_UNSUPPORTED = -5, /* d not 64/128, scale not finite and > 0, too large */
+    UA_ERR_HIP = -6          /* the HIP runtime reported an error              */
+};
+
+/*
+ * Fused path (abstract; Fig. 5 steps d-e; Fig. 7 piggybacked pipeline):
+ * attention over this rank's Hl heads, each output tile stored by the
+ * workgroup that computed it directly into its slot of `out`.
+ *   scale: softmax scale (the usual choice is 1/sqrt(d)); finite and > 0.
+ * B == 0 or S == 0 is a valid empty call (no launch, UA_OK).
+ */
+int attn_ulysses_fused(const void *Q, const void *K, const void *V, int rank, int P,
+                       void *out, const ua_shape *shp, float scale, void *stream);
+
+/*
+ * Serial baseline, attention half ("FlashAttention alone" in the abstract):
+ * the same attention kernel writing the head-partitioned O_local
+ * [B][S][Hl][d].  rank and P are validated like the fused call and fix Hl.
+ */
+int attn_serial(const void *Q, const void *K, const void *V, int rank, int P,
+                void *O_local, const ua_shape *shp, float scale, void *stream);
+
+/*
+ * Serial baseline, exchange half (the post-attention All-to-All of Fig. 5,
+ * run after attention as a separate step): copies every row of O_local
+ * [B][S][Hl][d] bit-for-bit into its slot of `out` [B][P][S/P][H][d].
+ * attn_serial followed by a2a_permute writes exactly the bytes
+ * attn_ulysses_fused writes.
+ */
+int a2a_permute(const void *O_local, int rank, int P, void *out,
+                const ua_shape *shp, void *stream);
+
+/* Static English text for a status code; never NULL. */
+const char *ua_status_string(int status);
+
+/* Bytes of the destination buffer, B*S*H*d*2 (0 if shp is NULL or invalid). */
+size_t ua_dest_bytes(const ua_shape *shp);
+
+/* Bytes of one rank's Q, K, V or O_local, B*S*(H/P)*d*2 (0 if invalid). */
+size_t ua_local_bytes(const ua_shape *shp, int P);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int ua_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_ATTN_H */

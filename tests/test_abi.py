@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+validates arguments on the host before any device access (CPU only: no call
+here reaches a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import comm_fusion_amd as ua
+from comm_fusion_amd._binding import Shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses_attn.h")
+
+A = 0x10000       # 16-byte aligned fake device addresses (never dereferenced:
+B_ = 0x20000      # every call below fails validation first)
+C = 0x30000
+O = 0x40000
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) >= {"attn_ulysses_fused", "attn_serial", "a2a_permute", "ua_status_string",
+                          "ua_dest_bytes", "ua_local_bytes", "ua_version"}
+    L = ctypes.CDLL(ua.lib_path())
+    for n in names:
+        assert hasattr(L, n), "missing export %s" % n
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, val in [("UA_OK", 0), ("UA_ERR_NULL", -1), ("UA_ERR_SHAPE", -2), ("UA_ERR_RANK", -3),
+                      ("UA_ERR_ALIGN", -4), ("UA_ERR_UNSUPPORTED", -5), ("UA_ERR_HIP", -6)]:
+        assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text)
+        assert getattr(ua, name) == val
+        assert ua.status_string(val) and ua.status_string(val) != "unknown status"
+    assert ua.status_string(12345) == "unknown status"
+    assert ua.version() == 10000
+
+
+def _fused(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
+    L = ua.lib()
+    return L.attn_ulysses_fused(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale, None)
+
+
+def _serial(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
+    L = ua.lib()
+    return L.attn_serial(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale, None)
+
+
+def _permute(shape, rank=0, P=2, src=A, out=O):
+    return ua.lib().a2a_permute(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
+
+
+@pytest.mark.parametrize("call", [_fused, _serial])
+def test_attention_argument_validation(call):
+    good = (1, 64, 4, 64)
+    assert ua.lib().attn_ulysses_fused(A, B_, C, 0, 2, O, None, 0.1, None) == ua.UA_ERR_NULL
+    assert call(good, q=0) == ua.UA_ERR_NULL
+    assert call(good, out=0) == ua.UA_ERR_NULL
+    assert call((1, 63, 4, 64)) == ua.UA_ERR_SHAPE        # S % P
+    assert call((1, 64, 5, 64)) == ua.UA_ERR_SHAPE        # H % P
+    assert call((-1, 64, 4, 64)) == ua.UA_ERR_SHAPE
+    assert call((1, 64, 0, 64)) == ua.UA_ERR_SHAPE
+    assert call(good, P=0) == ua.UA_ERR_SHAPE
+    assert call((1 << 40, 1 << 20, 4, 64)) == ua.UA_ERR_SHAPE  # byte size overflows
+    assert call(good, rank=2) == ua.UA_ERR_RANK
+    assert call(good, rank=-1) == ua.UA_ERR_RANK
+    assert call(good, k=B_ + 8) == ua.UA_ERR_ALIGN
+    assert call(good, out=O + 2) == ua.UA_ERR_ALIGN
+    assert call((1, 64, 4, 96)) == ua.UA_ERR_UNSUPPORTED
+    assert call(good, scale=0.0) == ua.UA_ERR_UNSUPPORTED
+    assert call(good, scale=-1.0) == ua.UA_ERR_UNSUPPORTED
+    assert call(good, scale=float("nan")) == ua.UA_ERR_UNSUPPORTED
+    assert call(good, scale=float("inf")) == ua.UA_ERR_UNSUPPORTED
+    assert call((1, 1 << 30, 8, 128), P=1) == ua.UA_ERR_UNSUPPORTED  # beyond grid limits
+
+
+@pytest.mark.parametrize("call", [_fused, _serial, _permute])
+def test_empty_calls_succeed_without_touching_memory(call):
+    assert call((0, 64, 4, 64), src=0, out=0) == ua.UA_OK if call is _permute else \
+        call((0, 64, 4, 64), q=0, k=0, v=0, out=0) == ua.UA_OK
+    assert call((3, 0, 4, 128), src=0, out=0) == ua.UA_OK if call is _permute else \
+        call((3, 0, 4, 128), q=0, k=0, v=0, out=0) == ua.UA_OK
+
+
+def test_permute_argument_validation():
+    good = (2, 64, 8, 128)
+    assert _permute(good, src=0) == ua.UA_ERR_NULL
+    assert _permute((2, 60, 8, 128), P=8) == ua.UA_ERR_SHAPE
+    assert _permute(good, rank=5, P=4) == ua.UA_ERR_RANK
+    assert _permute(good, src=A + 4) == ua.UA_ERR_ALIGN
+    assert _permute((2, 64, 8, 32)) == ua.UA_ERR_UNSUPPORTED
+
+
+def test_buffer_size_helpers():
+    assert ua.dest_bytes(2, 32768, 24, 64) == 2 * 32768 * 24 * 64 * 2
+    assert ua.local_bytes(2, 32768, 24, 64, 4) == 2 * 32768 * 6 * 64 * 2
+    assert ua.local_bytes(1, 8, 5, 64, 2) == 0     # H % P != 0
+    assert ua.dest_bytes(-1, 8, 4, 64) == 0
+    assert ua.lib().ua_dest_bytes(None) == 0

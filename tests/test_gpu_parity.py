@@ -1,0 +1,187 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Every test compares the library's output with ``oracle`` on the same seeded
+inputs: values within the stated tolerance, layout bit-exact (owned slots
+written, every other slot keeps the sentinel bits), and the bit-exact
+cross-checks that need no tolerance (permute vs the oracle's permutation,
+fused == permute(serial), run-to-run determinism).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import comm_fusion_amd as ua
+import oracle
+from gpu_helpers import (assert_close, bits_to_f64, check_dest_layout, empty_bf16, sentinel_buffer,
+                         to_dev, to_host_bits)
+from ua_inputs import SENTINEL_BITS, WORKLOADS, Workload, make_qkv, sampled_rows, workload_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _dev4(bits):
+    return to_dev(bits).view(*bits.shape)
+
+
+def _fused(Q, K, V, rank, P, H, scale=None):
+    B, S, Hl, d = Q.shape
+    dest = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused(_dev4(Q), _dev4(K), _dev4(V), rank, P, dest, scale)
+    _sync()
+    return to_host_bits(dest)
+
+
+def _serial(Q, K, V, rank, P, scale=None):
+    B, S, Hl, d = Q.shape
+    o = empty_bf16(Q.size).view(B, S, Hl, d)
+    ua.attn_serial(_dev4(Q), _dev4(K), _dev4(V), rank, P, o, scale)
+    _sync()
+    return o
+
+
+def _compare_rows(dest_bits, Q, K, V, rows, H, P, rank, scale, what):
+    B, S, Hl, d = Q.shape
+    ref = oracle.attn_rows(Q, K, V, scale, rows)
+    offs = oracle.dest_offsets(rows, B, S, H, d, P, rank)
+    assert np.all(offs >= 0)
+    got = bits_to_f64(dest_bits[offs[:, None] + np.arange(d)[None, :]])
+    return assert_close(got, ref, what)
+
+
+def _case(B, S, H, P, rank, d, seed):
+    Q, K, V = make_qkv(B, S, H // P, d, seed)
+    return Q, K, V
+
+
+# Small shapes spanning several Q/KV tiles, ragged tails (S not a multiple of
+# the 128-row Q tile or 64-key KV tile), regions that straddle Q tiles, both
+# head dims, P = 1 (identity placement) and S = P (one row per region).
+SMALL = [
+    # B, S, H, P, rank, d, seed
+    (1, 512, 4, 2, 0, 64, 0),      # the tiny workload
+    (1, 512, 4, 2, 1, 128, 1),
+    (2, 200, 8, 8, 3, 128, 2),     # ragged, regions of 25 rows
+    (1, 1, 1, 1, 0, 64, 3),        # single key
+    (1, 2, 2, 2, 1, 128, 4),       # S = P
+    (1, 3, 2, 1, 0, 64, 5),
+    (3, 130, 6, 2, 1, 64, 6),      # 130 = 2 Q tiles, 3 KV tiles (ragged)
+    (1, 384, 3, 3, 2, 128, 7),     # regions of 128 rows, 3 full Q tiles
+    (2, 96, 4, 4, 3, 128, 8),      # smaller than one Q tile
+]
+
+
+@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SMALL)
+def test_fused_matches_oracle_and_layout(B, S, H, P, rank, d, seed):
+    Q, K, V = _case(B, S, H, P, rank, d, seed)
+    scale = 1.0 / math.sqrt(d)
+    dest = _fused(Q, K, V, rank, P, H)
+    check_dest_layout(dest, B, S, H, d, P, rank)
+    rows = sampled_rows(Workload("t", B, S, H, P, rank, d, seed))
+    _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, "fused %s" % ((B, S, H, P, rank, d),))
+
+
+@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SMALL)
+def test_serial_matches_oracle(B, S, H, P, rank, d, seed):
+    Q, K, V = _case(B, S, H, P, rank, d, seed)
+    o = to_host_bits(_serial(Q, K, V, rank, P))
+    ref = oracle.attn_all(Q, K, V, 1.0 / math.sqrt(d))
+    assert_close(bits_to_f64(o).reshape(ref.shape), ref, "serial")
+
+
+@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SMALL)
+def test_permute_is_bit_exact_and_fused_equals_serial(B, S, H, P, rank, d, seed):
+    Q, K, V = _case(B, S, H, P, rank, d, seed)
+    o = _serial(Q, K, V, rank, P)
+    dest = sentinel_buffer(B * S * H * d)
+    ua.a2a_permute(o, rank, P, dest)
+    _sync()
+    got = to_host_bits(dest)
+    want = np.full(B * S * H * d, SENTINEL_BITS, np.uint16)
+    oracle.permute(to_host_bits(o).reshape(Q.shape), H, P, rank, want)
+    np.testing.assert_array_equal(got, want)
+    fused = _fused(Q, K, V, rank, P, H)
+    np.testing.assert_array_equal(fused, got)
+
+
+def test_permute_of_arbitrary_bits_is_exact():
+    # Not attention output: any 16-bit patterns, including NaN/Inf codes.
+    B, S, H, P, rank, d = 2, 96, 12, 4, 2, 64
+    rng = np.random.default_rng(50)
+    o = rng.integers(0, 1 << 16, size=(B, S, H // P, d), dtype=np.uint16)
+    dest = sentinel_buffer(B * S * H * d)
+    ua.a2a_permute(_dev4(o), rank, P, dest)
+    _sync()
+    want = np.full(B * S * H * d, SENTINEL_BITS, np.uint16)
+    oracle.permute(o, H, P, rank, want)
+    np.testing.assert_array_equal(to_host_bits(dest), want)
+
+
+def test_all_ranks_compose_to_full_multihead_attention():
+    # One global [B][S][H][d] problem; every rank runs on its head slice into
+    # the same destination.  Afterwards no sentinel remains and every row
+    # matches the oracle for its global head.
+    B, S, H, P, d = 2, 160, 8, 4, 64
+    Hl = H // P
+    Qg, Kg, Vg = make_qkv(B, S, H, d, 60)
+    dest = sentinel_buffer(B * S * H * d)
+    for r in range(P):
+        sl = np.s_[:, :, r * Hl:(r + 1) * Hl]
+        q, k, v = (np.ascontiguousarray(t[sl]) for t in (Qg, Kg, Vg))
+        ua.attn_ulysses_fused(_dev4(q), _dev4(k), _dev4(v), r, P, dest)
+    _sync()
+    got = to_host_bits(dest)
+    assert not np.any(got == SENTINEL_BITS)
+    ref = oracle.attn_all(Qg, Kg, Vg, 1.0 / math.sqrt(d))  # [B][S][H][d]
+    assert_close(bits_to_f64(got).reshape(ref.shape), ref, "all ranks")
+
+
+def test_runs_are_bitwise_deterministic():
+    Q, K, V = _case(2, 700, 8, 4, 1, 128, 70)
+    a = _fused(Q, K, V, 1, 4, 8)
+    b = _fused(Q, K, V, 1, 4, 8)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_uniform_v_and_zero_q_closed_forms():
+    B, S, H, P, rank, d = 1, 300, 4, 2, 1, 128
+    Q, K, _ = _case(B, S, H, P, rank, d, 80)
+    rng = np.random.default_rng(81)
+    from ua_inputs import to_bf16_bits
+    c = to_bf16_bits(rng.standard_normal((B, 1, H // P, d)).astype(np.float32))
+    V = np.ascontiguousarray(np.broadcast_to(c, Q.shape))
+    dest = _fused(Q, K, V, rank, P, H)
+    own = check_dest_layout(dest, B, S, H, d, P, rank)
+    assert_close(bits_to_f64(own), np.broadcast_to(bits_to_f64(c), own.shape), "uniform V")
+    # Q = 0: uniform weights, output = column mean of V.
+    _, K2, V2 = _case(B, S, H, P, rank, d, 82)
+    Z = np.zeros_like(K2)
+    dest = _fused(Z, K2, V2, rank, P, H)
+    own = check_dest_layout(dest, B, S, H, d, P, rank)
+    mean = bits_to_f64(V2).mean(axis=1, keepdims=True)
+    assert_close(bits_to_f64(own), np.broadcast_to(mean, own.shape), "Q = 0")
+
+
+def test_scale_is_applied():
+    Q, K, V = _case(1, 256, 2, 2, 0, 64, 90)
+    for scale in (0.02, 0.6):
+        dest = _fused(Q, K, V, 0, 2, 2, scale)
+        rows = sampled_rows(Workload("t", 1, 256, 2, 2, 0, 64, 90))
+        _compare_rows(dest, Q, K, V, rows, 2, 2, 0, scale, "scale %g" % scale)
+
+
+@pytest.mark.parametrize("name", ["dit_image", "dit_long", "video_dit", "mixed"])
+def test_workloads_at_full_size(name):
+    # The configurations the benchmark times, at full size: sampled rows
+    # against the oracle (all rows for DiT image) and a full-buffer layout scan.
+    w = WORKLOADS[name]
+    Q, K, V = workload_qkv(w)
+    dest = _fused(Q, K, V, w.rank, w.P, w.H)
+    check_dest_layout(dest, w.B, w.S, w.H, w.d, w.P, w.rank)
+    rows = sampled_rows(w)
+    _compare_rows(dest, Q, K, V, rows, w.H, w.P, w.rank, 1.0 / math.sqrt(w.d), name)
