@@ -1,0 +1,248 @@
+"""Benchmark: fused Ulysses-shard attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step = one attn_ulysses_fused call over the whole workload (attention over
+the rank's Hl heads, each output tile stored into its post-All-to-All slot).
+Inputs are seeded synthetic bf16 tensors already resident in HBM when timing
+starts.  Prints ONE JSON line:
+  value     attention TFLOP/s of the fused call, counting 4*S^2*d per
+            (batch, local head) (QK^T + PV, non-causal);
+  roofline  the fused attention kernel against the bf16 MFMA peak, from HIP
+            events around every launch on the launch stream;
+  detail    fused / serial (attention + separate permute) / attention-alone /
+            permute-alone times (medians over interleaved rounds), the
+            residual (fused - alone) / alone, the permute's HBM rate and the
+            fused epilogue's store volume;
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s + % bf16 MFMA peak; fused vs serial attn+A2A-permute time"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEFAULT_WORKLOAD = "video_dit"
+KERNEL_SOURCE = os.path.join(ROOT, "comm_fusion_amd", "csrc", "ua_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_video_dit_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the CPU oracle sample")
+    ap.add_argument("--rounds", type=int, default=5,
+                    help="interleaved rounds of fused / serial / alone / permute timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device-to-device copy of MIB MiB (a known-size "
+                         "kernel for scaling HBM byte counters under rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_launches(fn, steps, warmup):
+    """Per-launch durations (ms) from events recorded between back-to-back
+    launches on the current stream, plus the total (ms) over the K launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = _events(steps + 1)
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[steps]), wall
+
+
+def interleaved(fns, rounds, reps):
+    """Per-launch durations (ms) of several callables, timed in interleaved
+    rounds so that clock ramps and thermal drift hit all of them alike."""
+    import torch
+    out = {k: [] for k in fns}
+    for _ in range(rounds):
+        for name, fn in fns.items():
+            ev = _events(reps + 1)
+            ev[0].record()
+            for i in range(reps):
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            out[name] += [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return out
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_ms):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, only if it
+    was taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, Q, K, V, target_s):
+    """The fp64 oracle as it stands, on the host cores, over a bounded sample of
+    this workload's query rows (rows per second scaled to TFLOP/s)."""
+    import oracle
+    from ua_inputs import sampled_rows
+    rows = sampled_rows(dataclasses.replace(w, sampled=True))
+    scale = 1.0 / math.sqrt(w.d)
+    threads = oracle.max_threads()
+    flops_per_row = 4.0 * w.S * w.d
+    # calibrate on a small batch, then time a sample sized for ~target_s
+    probe = rows[: max(threads, 8)]
+    t0 = time.perf_counter()
+    oracle.attn_rows(Q, K, V, scale, probe)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(len(rows), max(len(probe), len(probe) * target_s / dt)))
+    reps = max(1, int(math.ceil(n / len(rows))))
+    sample = np.concatenate([rows] * reps)[:n] if n > len(rows) else rows[:n]
+    t0 = time.perf_counter()
+    oracle.attn_rows(Q, K, V, scale, sample)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops_per_row * len(sample) / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d query rows (of %d x %d) of the %s workload, full %d-key softmax each, fp64, %.1f s"
+                  % (len(sample), w.B * w.Hl, w.S, w.name, w.S, dt),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this path runs one Ulysses rank's share on "
+              "one MI355X (the P ranks are P regions of its HBM); --gpus %d is not supported"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import comm_fusion_amd as ua
+    from ua_inputs import SENTINEL_BITS, WORKLOADS, workload_qkv
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    Q, K, V = workload_qkv(w)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(Q), up(K), up(V)
+    n_dest = w.B * w.S * w.H * w.d
+    dest = torch.full((n_dest,), SENTINEL_BITS, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    o_local = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    fused = lambda: ua.attn_ulysses_fused(q, k, v, w.rank, w.P, dest)  # noqa: E731
+    alone = lambda: ua.attn_serial(q, k, v, w.rank, w.P, o_local)       # noqa: E731
+    perm = lambda: ua.a2a_permute(o_local, w.rank, w.P, dest)           # noqa: E731
+
+    def serial():
+        alone()
+        perm()
+
+    if args.calibrate_copy:
+        src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # The timed region: K fused steps back to back.
+    per, total_ms, wall_ms = time_launches(fused, args.steps, args.warmup)
+    # Baselines: fused, serial (attention + separate permute), attention
+    # alone and permute alone, in interleaved rounds.
+    reps = max(2, min(args.steps, int(200.0 / max(float(np.mean(per)), 1e-3)) + 1))
+    cmp = interleaved({"fused": fused, "serial": serial, "alone": alone, "perm": perm},
+                      args.rounds, reps)
+    per_serial, per_alone, per_perm = cmp["serial"], cmp["alone"], cmp["perm"]
+
+    ms_step = total_ms / args.steps
+    value = w.flops / (ms_step * 1e-3) / 1e12
+    launch_ms = float(np.mean(per))
+    achieved = w.flops / (launch_ms * 1e-3) / 1e12
+    med = lambda x: float(np.median(x))  # noqa: E731
+    t_f, t_s, t_a, t_p = med(cmp["fused"]), med(per_serial), med(per_alone), med(per_perm)
+    traffic = measured_traffic(launch_ms)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "P": w.P, "rank": w.rank,
+                   "d": w.d, "Hl": w.Hl, "flops_per_step": w.flops, "causal": False},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "detail": {
+            "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+            "fused_ms_median": round(t_f, 4), "fused_ms_min": round(min(cmp["fused"]), 4),
+            "timed_region_launch_ms_mean": round(launch_ms, 4),
+            "serial_ms_median": round(t_s, 4),
+            "attn_alone_ms_median": round(t_a, 4),
+            "permute_ms_median": round(t_p, 4),
+            "speedup_serial_over_fused": round(t_s / t_f, 4),
+            "residual_fused_vs_alone": round((t_f - t_a) / t_a, 4),
+            "hiding_ratio": round((t_s - t_f) / (t_s - t_a), 3) if t_s > t_a else None,
+            "permute_hbm_GBs": round(2 * w.out_bytes / (t_p * 1e-3) / 1e9, 1),
+            "epilogue_store_bytes": w.out_bytes,
+            "wall_ms_timed_region": round(wall_ms, 3),
+            "kernel_source_sha256_16": source_digest(),
+        },
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, Q, K, V, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -120,8 +120,13 @@ void attn_fwd(AttnArgs a)
     constexpr int DB = D / 32;            // 32-row blocks of O^T over d
     static_assert(NLD >= 1 && TILE % (kWaves * 1024) == 0, "tile split");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILE];
-    lds_u8 *const lds = (lds_u8 *)smem;
+    // Two K and two V tiles as four distinct arrays: the compiler can then
+    // tell the reads of one buffer from the asynchronous global->LDS writes
+    // into the other, and needs no wait on those writes mid-iteration.
+    __shared__ __attribute__((aligned(1024))) unsigned char k0s[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char k1s[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char v0s[TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char v1s[TILE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,7 +139,7 @@ void attn_fwd(AttnArgs a)
     const int h = bh % a.Hl;
     const int64_t b = bh / a.Hl;
     const int64_t S = a.S;
-    const int64_t rs = (int64_t)a.Hl * D;  // elements between sequence rows
+    const int rs = a.Hl * D;  // elements between sequence rows
     const int64_t head = (b * S * a.Hl + h) * D;
     const uint16_t *qh = a.q + head;
     const uint16_t *kh = a.k + head;
@@ -144,24 +149,41 @@ void attn_fwd(AttnArgs a)
     auto kswz = [](int row) { return (row / RPL) % CPR; };
     auto vswz = [](int row) { return 4 * ((row / RPL) % (CPR / 4)); };
 
-    // Copy KV tile starting at key kv0 into buffer buf.  Each wave moves NLD
-    // contiguous 1 KiB pieces of each tile; lane L of a piece lands at byte
-    // 16*L of it, so the lane picks the global chunk that belongs there.
-    // Keys past S read row S-1 (finite data, masked out of the softmax).
-    auto issue = [&](int64_t kv0, int buf) {
+    // Global->LDS copy of one KV tile: each wave moves NLD contiguous 1 KiB
+    // pieces of each tile; lane L of a piece lands at byte 16*L of it, so the
+    // lane fetches the global chunk that belongs there.  Per-lane element
+    // offsets within a full tile are fixed; only the tile base moves.
+    int koff[NLD], voff[NLD], lrow[NLD];
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int off = (wave * NLD + n) * 1024;
-            const int lin = off + lane * 16;
-            const int row = lin / RB;
-            const int pos = (lin % RB) >> 4;
-            int64_t gr = kv0 + row;
-            gr = gr < S ? gr : S - 1;
-            lds_u8 *kdst = lds + buf * 2 * TILE + off;
-            __builtin_amdgcn_global_load_lds((gbl_void *)(kh + gr * rs + (pos ^ kswz(row)) * 8),
-                                             (lds_void *)kdst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void *)(vh + gr * rs + (pos ^ vswz(row)) * 8),
-                                             (lds_void *)(kdst + TILE), 16, 0, 0);
+    for (int n = 0; n < NLD; ++n) {
+        const int lin = (wave * NLD + n) * 1024 + lane * 16;
+        const int row = lin / RB;
+        const int pos = (lin % RB) >> 4;
+        lrow[n] = row;
+        koff[n] = row * rs + (pos ^ kswz(row)) * 8;
+        voff[n] = row * rs + (pos ^ vswz(row)) * 8;
+    }
+    auto issue = [&](int64_t kv0, lds_u8 *kd, lds_u8 *vd) {
+        const uint16_t *kb = kh + kv0 * rs;
+        const uint16_t *vb = vh + kv0 * rs;
+        if (kv0 + kBn <= S) {
+#pragma unroll
+            for (int n = 0; n < NLD; ++n) {
+                const int off = (wave * NLD + n) * 1024;
+                __builtin_amdgcn_global_load_lds((gbl_void *)(kb + koff[n]), (lds_void *)(kd + off), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_void *)(vb + voff[n]), (lds_void *)(vd + off), 16, 0, 0);
+            }
+        } else {
+            // Last, partial tile: keys past S read row S-1 (finite data,
+            // masked out of the softmax).
+            const int last = (int)(S - 1 - kv0);
+#pragma unroll
+            for (int n = 0; n < NLD; ++n) {
+                const int off = (wave * NLD + n) * 1024;
+                const int shift = (lrow[n] > last ? last - lrow[n] : 0) * rs;
+                __builtin_amdgcn_global_load_lds((gbl_void *)(kb + koff[n] + shift), (lds_void *)(kd + off), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_void *)(vb + voff[n] + shift), (lds_void *)(vd + off), 16, 0, 0);
+            }
         }
     };
 
@@ -183,20 +205,22 @@ void attn_fwd(AttnArgs a)
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_run = -INFINITY;  // running max of raw scores of this row
-    float l_run = 0.f;        // this lane's part of the running row sum
+    // Running max of this row's scaled scores (log2 domain).  It is only a
+    // stabiliser: it is raised when a tile's max exceeds it by more than 8
+    // (a factor 256), so P stays below 2^8 and O rarely needs rescaling;
+    // the final O / l is the same for any choice of it.
+    float m_run = -INFINITY;
+    float l_run = 0.f;  // this lane's part of the running row sum
 
-    issue(0, 0);
-    for (int t = 0; t < ntiles; ++t) {
-        const int buf = t & 1;
+    const int i16 = lane & 15;
+    const int half = (lane >> 4) & 1;
+
+    auto step = [&](int t, const lds_u8 *kt, const lds_u8 *vt, lds_u8 *kn, lds_u8 *vn) {
         // Tile t has landed for this wave; the barrier makes every wave's
         // part visible and ends all reads of the other buffer.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (t + 1 < ntiles) issue((int64_t)(t + 1) * kBn, buf ^ 1);
-
-        const lds_u8 *kt = lds + buf * 2 * TILE;
-        const lds_u8 *vt = kt + TILE;
+        if (t + 1 < ntiles) issue((int64_t)(t + 1) * kBn, kn, vn);
 
         // ---- S^T (64 keys x 32 queries) = K_t Q^T.  A operand: lane reads
         // K row jb*32 + il, d-chunk 2kk+g (16 B); the XOR swizzle spreads the
@@ -219,38 +243,41 @@ void attn_fwd(AttnArgs a)
         // Accumulator element r of block jb is key kv0 + jb*32 + 8(r/4) + 4g + r%4.
         const int64_t kv0 = (int64_t)t * kBn;
         if (kv0 + kBn > S) {
+            const int lim = (int)(S - kv0);
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (kv0 + jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= S) sacc[jb][r] = -INFINITY;
+                    if (jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= lim) sacc[jb][r] = -INFINITY;
         }
 
-        // ---- online softmax (fp32).
+        // ---- online softmax (fp32, log2 domain).
         float mt = sacc[0][0];
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[jb][r]);
-        mt = row_max(mt);
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-        m_run = m_new;
-        const float mb = m_new * c;
-        float ls = 0.f;
+        mt = row_max(mt) * c;
+        const bool raise = mt > m_run + 8.0f;  // same in both lanes of a row
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+            const float m_new = raise ? mt : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 if kept, 0 at start
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float mb = m_run;
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jb][r], c, -mb));
                 sacc[jb][r] = p;
-                ls += p;
+                l_run += p;
             }
-        l_run = fmaf(l_run, alpha, ls);
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 
         // ---- O^T (d x 32 queries) += V_t^T P^T, four 16-key chunks.
         // B operand (P^T): chunk cc takes registers 8(cc%2)..+7 of block cc/2,
@@ -259,8 +286,6 @@ void attn_fwd(AttnArgs a)
         // transposing reads, each giving 4 consecutive keys: in a 16-lane
         // group, source lane i16 points at V row (k0 + i16/4), columns
         // dd0 + 4(i16%4) .. +3, and result lane i16 gets column dd0 + i16.
-        const int i16 = lane & 15;
-        const int half = (lane >> 4) & 1;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             u32x4 pb;
@@ -286,6 +311,16 @@ void attn_fwd(AttnArgs a)
                     0);
             }
         }
+    };
+
+    lds_u8 *const K0 = (lds_u8 *)k0s;
+    lds_u8 *const K1 = (lds_u8 *)k1s;
+    lds_u8 *const V0 = (lds_u8 *)v0s;
+    lds_u8 *const V1 = (lds_u8 *)v1s;
+    issue(0, K0, V0);
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, K0, V0, K1, V1);
+        if (t + 1 < ntiles) step(t + 1, K1, V1, K0, V0);
     }
 
     // ---- epilogue: normalise and store this lane's half of its row straight

@@ -35,8 +35,11 @@
  *
  * Errors: every call returns a status code and never prints or aborts.
  * Arguments are validated on the host before any device access, in this
- * order: null pointers, shape, rank, alignment, support; a launch failure
- * reported by the runtime gives UA_ERR_HIP.
+ * order: shp NULL (UA_ERR_NULL); shape (UA_ERR_SHAPE); rank (UA_ERR_RANK);
+ * head dim, scale and launch-size limits (UA_ERR_UNSUPPORTED); then an empty
+ * call (B == 0 or S == 0) returns UA_OK without touching any pointer;
+ * otherwise NULL buffers (UA_ERR_NULL) and alignment (UA_ERR_ALIGN).  A
+ * launch failure reported by the runtime gives UA_ERR_HIP.
  */
 #ifndef ULYSSES_ATTN_H
 #define ULYSSES_ATTN_H
