@@ -9,30 +9,37 @@
 // output-tile owner issues the exchange stores itself, then moves on).
 //
 // Design for CDNA4, not a translation of the pages' FlashAttention-3/4:
-//  * one workgroup = 4 wave64s = one work unit of 128 query rows of one
-//    (batch, local head); each wave owns 32 query rows;
+//  * a workgroup of NW wave64s (8, or 4 for small problems) owns 32*NW query
+//    rows of one (batch, local head); each wave owns 32 rows.  All waves
+//    share each K/V tile, so a tile crosses L2 -> LDS once per 32*NW rows;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K streams from LDS as the A operand and the
 //    wave's Q rows stay in VGPRs as the B operand.  The accumulator layout
-//    then gives every lane ONE query row (lane % 32) and 16 keys, so the
-//    row max needs one cross-half swap (v_permlane32_swap) per KV tile and
-//    the row sum none until the end;
-//  * P^T is fed from those same registers (rounded to bf16) as the B operand
-//    of O^T += V^T P^T; V^T comes from the row-major V tile through the
-//    gfx950 transposing LDS read ds_read_b64_tr_b16;
+//    then gives every lane ONE query row (lane % 32) and 16 keys per block,
+//    so the row max needs one v_permlane32_swap per KV tile and the row sum
+//    none until the end;
+//  * P^T is fed from those registers (rounded to bf16) as the B operand of
+//    O^T += V^T P^T; V^T comes from the key-major V tile through the gfx950
+//    transposing LDS read ds_read_b64_tr_b16;
 //  * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4
-//    (no VGPR staging), double buffered; both tiles are XOR-swizzled in
-//    16-byte chunks so the MFMA operand reads are free of bank conflicts;
-//  * online softmax in fp32 with exp2 (log2 e folded into the scale);
+//    (no VGPR staging), double buffered, one tile ahead;
+//  * software pipeline: in steady state, iteration t interleaves the
+//    softmax of S_t with the MFMAs of O += V_{t-1} P_{t-1} and of S_{t+1},
+//    one MFMA plus a slice of softmax VALU work per issue slot, so every
+//    wave keeps its matrix pipe fed while it does its exponentials;
+//  * online softmax in fp32, log2 domain, with a lazily raised running max;
 //  * epilogue: each lane normalises its row and stores it straight to the
 //    destination slot computed from (rank, P) -- the fused All-to-All.  The
-//    local (serial) output is the same epilogue with one region.
+//    local (serial) output is the same epilogue with one region;
 //  * workgroup ids are remapped so that consecutive work units of one head
 //    run on the same XCD and share its L2 while they stream the same K/V.
 
 #include "ua_internal.h"
 
 #include <math.h>
+
+#include <type_traits>
+#include <utility>
 
 namespace ua {
 namespace {
@@ -51,10 +58,10 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-constexpr int kWaves = 4;             // waves per workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBr = 32 * kWaves;      // query rows per work unit
-constexpr int kBn = 64;               // keys per KV tile
+constexpr int kBn = 64;        // keys per KV tile
+constexpr int kNB = kBn / 32;  // 32-key blocks per KV tile
+constexpr int kPF = 2;         // operand prefetch distance, in MFMAs
+constexpr int kRowsPerWave = 32;
 
 struct AttnArgs {
     const uint16_t *q;
@@ -96,6 +103,46 @@ __device__ __forceinline__ float row_sum(float x)
     return p[0] + p[1];
 }
 
+// MFMA operand reads from LDS in the steady-state loop, as explicit
+// instructions with compile-time offsets.  The compiler does not track them,
+// so it inserts no waits for them -- in particular none on the asynchronous
+// global->LDS copies into the other buffer, which it cannot tell apart from
+// these reads -- and each read is waited for exactly, with lgkm_wait, right
+// before the MFMA that consumes it.  No compiler-visible LDS or scalar-memory
+// operation is in flight while these are (every steady iteration ends with
+// all of them complete).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(unsigned addr)
+{
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr16(unsigned addr)
+{
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+// Wait until at most N LDS reads are outstanding; tied to the fragment so the
+// compiler cannot move the fragment's consumer above the wait.
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4 &f)
+{
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "i"(N));
+}
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(std::make_integer_sequence<int, N>(), f);
+}
+
 // Logical work unit of this workgroup.  Workgroup i is dispatched to XCD
 // i % 8; give each XCD a contiguous run of units (same head, neighbouring Q
 // tiles) so they share K/V in that XCD's L2.  A bijection on [0, n).
@@ -106,32 +153,43 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
-template <int D>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(2, 2)))
+// NW = 8: two waves per SIMD, one workgroup per CU.  NW = 4 only runs for
+// shapes with fewer work units than CUs, so it is built for one wave per SIMD
+// (and gets that SIMD's whole register file).
+template <int D, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd(AttnArgs a)
 {
-    constexpr int RB = D * 2;             // bytes per K/V row
-    constexpr int CPR = D / 8;            // 16-byte chunks per row
-    constexpr int RPL = 256 / RB;         // rows per 256-byte LDS bank line
-    constexpr int TILE = kBn * RB;        // bytes of one K (or V) tile
-    constexpr int NLD = TILE / (kWaves * 1024);  // 1 KiB global->LDS copies per wave
-    constexpr int KK = D / 16;            // MFMA k-steps over d for S^T
-    constexpr int DB = D / 32;            // 32-row blocks of O^T over d
-    static_assert(NLD >= 1 && TILE % (kWaves * 1024) == 0, "tile split");
+    constexpr int TILE = kBn * D * 2;        // bytes of one K (or V) tile
+    constexpr int NLD = TILE / (NW * 1024);  // 1 KiB global->LDS copies per wave
+    constexpr int KK = D / 16;               // MFMA k-steps over d for S^T
+    constexpr int DB = D / 32;               // 32-row blocks of O^T over d
+    constexpr int GB = kBn * 64;             // bytes of one 32-column group of a tile
+    constexpr int BR = kRowsPerWave * NW;    // query rows per work unit
+    static_assert(NLD >= 1 && TILE % (NW * 1024) == 0, "tile split");
 
-    // Two K and two V tiles as four distinct arrays: the compiler can then
-    // tell the reads of one buffer from the asynchronous global->LDS writes
-    // into the other, and needs no wait on those writes mid-iteration.
+    // Two K and two V tiles as four distinct arrays, selected at compile
+    // time, so that the compiler-visible reads of one buffer (prologue and
+    // last iterations) never wait on the asynchronous writes into the other.
     __shared__ __attribute__((aligned(1024))) unsigned char k0s[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char k1s[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char v0s[TILE];
     __shared__ __attribute__((aligned(1024))) unsigned char v1s[TILE];
+    auto Kb = [&](auto j) -> lds_u8 * {
+        if constexpr (decltype(j)::value == 0) return (lds_u8 *)k0s; else return (lds_u8 *)k1s;
+    };
+    auto Vb = [&](auto j) -> lds_u8 * {
+        if constexpr (decltype(j)::value == 0) return (lds_u8 *)v0s; else return (lds_u8 *)v1s;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int il = lane & 31;  // query row of this lane within the wave
     const int g = lane >> 5;   // half-wave
+    const int i16 = lane & 15;
+    const int half = (lane >> 4) & 1;
 
     const int unit = xcd_unit(blockIdx.x, a.n_units);
     const int qt = unit % a.n_qtiles;
@@ -145,51 +203,50 @@ void attn_fwd(AttnArgs a)
     const uint16_t *kh = a.k + head;
     const uint16_t *vh = a.v + head;
 
-    // Swizzles (16-byte chunk index XOR), see the operand reads below.
-    auto kswz = [](int row) { return (row / RPL) % CPR; };
-    auto vswz = [](int row) { return 4 * ((row / RPL) % (CPR / 4)); };
-
-    // Global->LDS copy of one KV tile: each wave moves NLD contiguous 1 KiB
-    // pieces of each tile; lane L of a piece lands at byte 16*L of it, so the
-    // lane fetches the global chunk that belongs there.  Per-lane element
-    // offsets within a full tile are fixed; only the tile base moves.
-    int koff[NLD], voff[NLD], lrow[NLD];
+    // LDS tile layouts (filled by whole-wave 1 KiB global->LDS copies, lane
+    // L of a copy landing at byte 16*L, so a layout is just a per-lane choice
+    // of the global chunk to fetch):
+    //   K tile: [group of 32 columns][key row][64 B], the four 16 B chunks of
+    //     a row segment stored in the order chunk ^ ((row / 4) % 4), so the
+    //     S^T operand read (16 rows, one chunk per quarter-wave) hits 16
+    //     distinct 16 B bank slots;
+    //   V tile: [group of 32 columns][key row][64 B]; a transposing read
+    //     (8 rows x 64 B of one group per wave) is 512 contiguous bytes.
+    // Each copy fetches 16 row segments of 64 contiguous bytes: 1 KiB copy
+    // number c (wave-uniform) covers group c / 4, rows 16*(c % 4) .. +15, and
+    // lane L takes row 16*(c % 4) + L/4, 16 B chunk L % 4 of the segment.  The
+    // row's swizzle (row / 4) % 4 is then (L / 16) % 4 for every copy, so
+    // only these per-lane parts live in VGPRs.
+    static_assert(GB == 4 * 1024, "four 1 KiB copies per column group");
+    const int lrow = lane >> 2;
+    const int k_src = lrow * rs + ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+    const int v_src = lrow * rs + (lane & 3) * 8;
+    // Keys past S (last, partial tile) read row S-1: finite data that the
+    // softmax masks out.
+    auto tile_copy = [&](const uint16_t *src, int lane_src, int64_t kv0, lds_u8 *dst) {
+        const uint16_t *base = src + kv0 * rs + lane_src;
+        const int last = (int)(S - 1 - kv0);  // last valid row of the tile
 #pragma unroll
-    for (int n = 0; n < NLD; ++n) {
-        const int lin = (wave * NLD + n) * 1024 + lane * 16;
-        const int row = lin / RB;
-        const int pos = (lin % RB) >> 4;
-        lrow[n] = row;
-        koff[n] = row * rs + (pos ^ kswz(row)) * 8;
-        voff[n] = row * rs + (pos ^ vswz(row)) * 8;
-    }
-    auto issue = [&](int64_t kv0, lds_u8 *kd, lds_u8 *vd) {
-        const uint16_t *kb = kh + kv0 * rs;
-        const uint16_t *vb = vh + kv0 * rs;
-        if (kv0 + kBn <= S) {
-#pragma unroll
-            for (int n = 0; n < NLD; ++n) {
-                const int off = (wave * NLD + n) * 1024;
-                __builtin_amdgcn_global_load_lds((gbl_void *)(kb + koff[n]), (lds_void *)(kd + off), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((gbl_void *)(vb + voff[n]), (lds_void *)(vd + off), 16, 0, 0);
-            }
-        } else {
-            // Last, partial tile: keys past S read row S-1 (finite data,
-            // masked out of the softmax).
-            const int last = (int)(S - 1 - kv0);
-#pragma unroll
-            for (int n = 0; n < NLD; ++n) {
-                const int off = (wave * NLD + n) * 1024;
-                const int shift = (lrow[n] > last ? last - lrow[n] : 0) * rs;
-                __builtin_amdgcn_global_load_lds((gbl_void *)(kb + koff[n] + shift), (lds_void *)(kd + off), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((gbl_void *)(vb + voff[n] + shift), (lds_void *)(vd + off), 16, 0, 0);
-            }
+        for (int n = 0; n < NLD; ++n) {
+            const int cp = wave * NLD + n;
+            const int row0 = 16 * (cp & 3);
+            const uint16_t *p = base + row0 * rs + (cp >> 2) * 32;
+            if (kv0 + kBn > S && row0 + lrow > last) p -= (row0 + lrow - last) * rs;
+            __builtin_amdgcn_global_load_lds((gbl_void *)p, (lds_void *)(dst + cp * 1024), 16, 0, 0);
         }
     };
+    auto copy_k = [&](int t, lds_u8 *dst) { tile_copy(kh, k_src, (int64_t)t * kBn, dst); };
+    auto copy_v = [&](int t, lds_u8 *dst) { tile_copy(vh, v_src, (int64_t)t * kBn, dst); };
+    // All of this wave's copies have landed; after the barrier every wave's
+    // have, and no wave still reads the buffers the next copies overwrite.
+    auto sync_tiles = [&]() {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
 
-    // This lane's query row; rows past S (ragged last tile) compute on row
+    // This lane's query row; rows past S (ragged last Q tile) compute on row
     // S-1 and are not stored.
-    const int64_t s_q = (int64_t)qt * kBr + wave * 32 + il;
+    const int64_t s_q = (int64_t)qt * BR + wave * kRowsPerWave + il;
     const int64_t s_ld = s_q < S ? s_q : S - 1;
 
     // B operand of S^T = K Q^T: lane holds Q[s][16kk + 8g .. +7].
@@ -198,129 +255,287 @@ void attn_fwd(AttnArgs a)
     for (int kk = 0; kk < KK; ++kk)
         qf[kk] = *(const u32x4 *)(qh + s_ld * rs + 16 * kk + 8 * g);
 
-    const int ntiles = (int)((S + kBn - 1) / kBn);
-    const float c = a.scale_log2;
+    // ---- S^T (64 keys x 32 queries) = K_t Q^T.  A operand: lane reads K row
+    // jb*32 + il, d-chunk 2kk+g (16 B).  Accumulator element r of block jb is
+    // key jb*32 + 8(r/4) + 4g + r%4 of the tile, query il.  (Prologue and
+    // first iteration; the steady loop issues the same products itself.)
+    auto qk = [&](const lds_u8 *kt, f32x16 (&s)[kNB]) {
+#pragma unroll
+        for (int jb = 0; jb < kNB; ++jb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
+            const int row = jb * 32 + il;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int sub = (2 * (kk & 1) + g) ^ ((row >> 2) & 3);
+                const u32x4 kf = *(const lds_u32x4 *)(kt + (kk >> 1) * GB + row * 64 + sub * 16);
+                s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                                __builtin_bit_cast(bf16x8, qf[kk]),
+                                                                s[jb], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- O^T (d x 32 queries) += V_t^T P_t^T, in 16-key chunks.
+    // B operand (P^T): chunk cc holds registers 8(cc%2)..+7 of block cc/2,
+    // i.e. element e is key 16cc + 8(e/4) + 4g + e%4.
+    // A operand (V^T): lane needs V[those keys][db*32 + lane%32]; two
+    // transposing reads, each giving 4 consecutive keys: in a 16-lane group,
+    // source lane i16 points at V row (k0 + i16/4), columns dd0 + 4(i16%4)
+    // .. +3 (dd0 = db*32 + 16*half), and result lane i16 gets column dd0+i16.
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    // Running max of this row's scaled scores (log2 domain).  It is only a
-    // stabiliser: it is raised when a tile's max exceeds it by more than 8
-    // (a factor 256), so P stays below 2^8 and O rarely needs rescaling;
-    // the final O / l is the same for any choice of it.
-    float m_run = -INFINITY;
-    float l_run = 0.f;  // this lane's part of the running row sum
-
-    const int i16 = lane & 15;
-    const int half = (lane >> 4) & 1;
-
-    auto step = [&](int t, const lds_u8 *kt, const lds_u8 *vt, lds_u8 *kn, lds_u8 *vn) {
-        // Tile t has landed for this wave; the barrier makes every wave's
-        // part visible and ends all reads of the other buffer.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (t + 1 < ntiles) issue((int64_t)(t + 1) * kBn, kn, vn);
-
-        // ---- S^T (64 keys x 32 queries) = K_t Q^T.  A operand: lane reads
-        // K row jb*32 + il, d-chunk 2kk+g (16 B); the XOR swizzle spreads the
-        // 16 rows a quarter-wave reads over all banks.
-        f32x16 sacc[2];
+    const int v_lane = (4 * g + (i16 >> 2)) * 64 + (16 * half + 4 * (i16 & 3)) * 2;
+    auto pv = [&](const lds_u8 *vt, const u32x4 (&pb)[2 * kNB]) {
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[jb][r] = 0.f;
-            const int row = jb * 32 + il;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int pos = (2 * kk + g) ^ kswz(row);
-                const u32x4 kf = *(const lds_u32x4 *)(kt + row * RB + pos * 16);
-                sacc[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[kk]), sacc[jb],
-                    0, 0, 0);
-            }
-        }
-        // Accumulator element r of block jb is key kv0 + jb*32 + 8(r/4) + 4g + r%4.
-        const int64_t kv0 = (int64_t)t * kBn;
-        if (kv0 + kBn > S) {
-            const int lim = (int)(S - kv0);
-#pragma unroll
-            for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= lim) sacc[jb][r] = -INFINITY;
-        }
-
-        // ---- online softmax (fp32, log2 domain).
-        float mt = sacc[0][0];
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[jb][r]);
-        mt = row_max(mt) * c;
-        const bool raise = mt > m_run + 8.0f;  // same in both lanes of a row
-        if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-            const float m_new = raise ? mt : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 1 if kept, 0 at start
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        }
-        const float mb = m_run;
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[jb][r], c, -mb));
-                sacc[jb][r] = p;
-                l_run += p;
-            }
-
-        // ---- O^T (d x 32 queries) += V_t^T P^T, four 16-key chunks.
-        // B operand (P^T): chunk cc takes registers 8(cc%2)..+7 of block cc/2,
-        // i.e. element e is key 16cc + 8(e/4) + 4g + e%4.
-        // A operand (V^T): lane needs V[those keys][db*32 + lane%32]; two
-        // transposing reads, each giving 4 consecutive keys: in a 16-lane
-        // group, source lane i16 points at V row (k0 + i16/4), columns
-        // dd0 + 4(i16%4) .. +3, and result lane i16 gets column dd0 + i16.
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            u32x4 pb;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2)
-                pb[e2] = pack_bf16(sacc[cc >> 1][8 * (cc & 1) + 2 * e2],
-                                   sacc[cc >> 1][8 * (cc & 1) + 2 * e2 + 1]);
-            const int row1 = 16 * cc + 4 * g + (i16 >> 2);
-            const int row2 = row1 + 8;
+        for (int cc = 0; cc < 2 * kNB; ++cc)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int dd = db * 32 + 16 * half + 4 * (i16 & 3);
-                const int ch = dd >> 3, within = (dd & 7) * 2;
-                const lds_u8 *p1 = vt + row1 * RB + ((ch ^ vswz(row1)) << 4) + within;
-                const lds_u8 *p2 = vt + row2 * RB + ((ch ^ vswz(row2)) << 4) + within;
+                const lds_u8 *p1 = vt + db * GB + 16 * cc * 64 + v_lane;
                 const u32x2 a1 = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1));
                 const u32x2 a2 = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p2));
+                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p1 + 8 * 64)));
                 const u32x4 af = {a1[0], a1[1], a2[0], a2[1]};
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, pb), oacc[db], 0, 0,
-                    0);
+                    __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, pb[cc]), oacc[db],
+                    0, 0, 0);
             }
-        }
     };
 
-    lds_u8 *const K0 = (lds_u8 *)k0s;
-    lds_u8 *const K1 = (lds_u8 *)k1s;
-    lds_u8 *const V0 = (lds_u8 *)v0s;
-    lds_u8 *const V1 = (lds_u8 *)v1s;
-    issue(0, K0, V0);
-    for (int t = 0; t < ntiles; t += 2) {
-        step(t, K0, V0, K1, V1);
-        if (t + 1 < ntiles) step(t + 1, K1, V1, K0, V0);
+    // ---- online softmax in the log2 domain.  m_run is the running max of
+    // this row's scaled scores.  It is only a stabiliser: it is raised when a
+    // tile's max exceeds it by more than 8 (a factor 256), so P stays below
+    // 2^8 and O rarely needs rescaling; O / l comes out the same for any
+    // choice of it.  l_run is this lane's part of the row sum, taken over the
+    // same bf16-rounded P that feeds the PV product.
+    const float c = a.scale_log2;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // Raise decision for a tile whose scaled max is mt.  Returns true (for
+    // the whole wave) when some row raised its max; O must then be multiplied
+    // by alpha once the previous tile's PV product has been added.
+    auto raise_max = [&](float mt, float &alpha) -> bool {
+        const bool raise = mt > m_run + 8.0f;  // same in both lanes of a row
+        const float m_new = raise ? mt : m_run;
+        alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exactly 1 when kept, 0 at the start
+        m_run = m_new;
+        l_run *= alpha;
+        return __builtin_amdgcn_ballot_w64(raise) != 0;
+    };
+    auto softmax_max = [&](f32x16 (&s)[kNB], int valid, float &alpha) -> bool {
+        if (valid < kBn) {
+#pragma unroll
+            for (int jb = 0; jb < kNB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= valid) s[jb][r] = -INFINITY;
+        }
+        // two independent chains keep the max reduction short
+        float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[0][2], s[0][3]);
+#pragma unroll
+        for (int jb = 0; jb < kNB; ++jb)
+#pragma unroll
+            for (int r = (jb == 0 ? 4 : 0); r < 16; r += 2) {
+                m0 = fmaxf(m0, s[jb][r]);
+                m1 = fmaxf(m1, s[jb][r + 1]);
+            }
+        return raise_max(row_max(fmaxf(m0, m1)) * c, alpha);
+    };
+    // P for two neighbouring keys of chunk cc, rounded to bf16 and packed as
+    // the B operand of the PV product; the row sum takes the rounded values.
+    auto exp_pair = [&](const f32x16 (&s)[kNB], u32x4 (&pb)[2 * kNB], int cc, int e2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * e2], c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * e2 + 1], c, -m_run));
+        f32x2 f = {p0, p1};
+        const bf16x2 hb = __builtin_convertvector(f, bf16x2);
+        pb[cc][e2] = __builtin_bit_cast(unsigned, hb);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(hb, ones, l_run, false);
+    };
+    auto softmax_exp = [&](const f32x16 (&s)[kNB], u32x4 (&pb)[2 * kNB]) {
+#pragma unroll
+        for (int cc = 0; cc < 2 * kNB; ++cc)
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) exp_pair(s, pb, cc, e2);
+    };
+    auto rescale_o = [&](float alpha) {
+        asm volatile("");  // keeps this off the common path (no if-conversion)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    };
+
+    // ---- software pipeline over KV tiles.  Iteration t: softmax of S_t
+    // interleaves with the MFMAs of PV_{t-1} and of S_{t+1}; tile copies run
+    // one iteration ahead (K_{t+2} and V_t are copied during iteration t).
+    // K_j and V_j live in buffer j % 2.
+    const int ntiles = (int)((S + kBn - 1) / kBn);
+    const int valid_last = (int)(S - (int64_t)(ntiles - 1) * kBn);
+    f32x16 sA[kNB], sB[kNB];         // S of even / odd tiles
+    u32x4 pA[2 * kNB], pB[2 * kNB];  // packed P of even / odd tiles
+
+    // Steady iteration with an explicit issue order.  Slot m issues the LDS
+    // reads for MFMA m + kPF, MFMA m, and a fixed slice of the softmax VALU
+    // work; scheduling fences keep the compiler from gathering the VALU work
+    // into one block (a wave whose MFMAs run back to back while its VALU
+    // work sits in one block leaves the matrix pipe idle during that block).
+    //   MFMA order: PV_{t-1} (chunk cc, block db), then S_{t+1} (block jb,
+    //   k-step kk).  VALU order: tile max of S_t in NMX slots, then the
+    //   raise step, then EPS exp pairs per slot.
+    constexpr int NPV = 2 * kNB * DB;
+    constexpr int NS = kNB * KK;
+    constexpr int NM = NPV + NS;
+    constexpr int NMX = 2 * kNB;  // max slots, 8 values each
+    constexpr int NEX = 8 * kNB;  // exp pairs
+    constexpr int EPS = (NEX + (NM - NMX - 1) - 1) / (NM - NMX - 1);
+    static_assert(NM > NMX + 1, "no slots left for the exp pairs");
+    // Per-lane LDS byte offsets of the steady-state operand reads: K row il
+    // of a 32-row block, 16 B chunk (2*(kk%2) + g) ^ ((il/4)%4); the rest of
+    // each address is a compile-time offset plus the buffer base.
+    const unsigned k_lane0 = il * 64 + (((0 + g) ^ ((il >> 2) & 3)) * 16);
+    const unsigned k_lane1 = il * 64 + (((2 + g) ^ ((il >> 2) & 3)) * 16);
+    constexpr int NRD_PV = 2, NRD_S = 1;  // LDS reads per MFMA fragment
+    // reads issued after fragment m's and before MFMA m (fragments m+1 .. m+kPF)
+    auto after = [](int m) constexpr {
+        int n = 0;
+        for (int j = m + 1; j <= m + kPF && j < NM; ++j) n += j < NPV ? NRD_PV : NRD_S;
+        return n;
+    };
+    auto load_frag = [&](auto mc, u32x4 &dst, unsigned vbase, unsigned kbase) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m < NPV) {
+            constexpr int cc = m / DB, db = m % DB;
+            constexpr int off = db * GB + 16 * cc * 64;
+            const u32x2 a1 = lds_tr16<off>(vbase + v_lane);
+            const u32x2 a2 = lds_tr16<off + 8 * 64>(vbase + v_lane);
+            dst = u32x4{a1[0], a1[1], a2[0], a2[1]};
+        } else {
+            constexpr int q = m - NPV, jb = q / KK, kk = q % KK;
+            constexpr int off = (kk >> 1) * GB + jb * 32 * 64;
+            dst = lds_b128<off>(kbase + ((kk & 1) ? k_lane1 : k_lane0));
+        }
+    };
+    auto steady = [&](int t, auto par) {
+        constexpr int P = decltype(par)::value;  // t % 2
+        using IP = std::integral_constant<int, P>;
+        using IQ = std::integral_constant<int, 1 - P>;
+        f32x16 (&s_cur)[kNB] = P ? sB : sA;
+        f32x16 (&s_nxt)[kNB] = P ? sA : sB;
+        u32x4 (&p_cur)[2 * kNB] = P ? pB : pA;
+        u32x4 (&p_prv)[2 * kNB] = P ? pA : pB;
+        const unsigned vbase = (unsigned)(uintptr_t)Vb(IQ());
+        const unsigned kbase = (unsigned)(uintptr_t)Kb(IQ());
+        sync_tiles();
+        if (t + 2 < ntiles) copy_k(t + 2, Kb(IP()));
+        copy_v(t, Vb(IP()));
+        u32x4 fr[kPF + 1];
+        static_for<kPF>([&](auto mc) { load_frag(mc, fr[decltype(mc)::value], vbase, kbase); });
+        float mx[NMX];
+        float alpha = 1.f;
+        bool any = false;
+        static_for<NM>([&](auto mc) {
+            constexpr int m = decltype(mc)::value;
+            if constexpr (m + kPF < NM)
+                load_frag(std::integral_constant<int, m + kPF>(), fr[(m + kPF) % (kPF + 1)], vbase, kbase);
+            u32x4 f = fr[m % (kPF + 1)];
+            lgkm_wait<after(m)>(f);
+            if constexpr (m < NPV) {
+                constexpr int cc = m / DB, db = m % DB;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, f), __builtin_bit_cast(bf16x8, p_prv[cc]), oacc[db], 0, 0, 0);
+            } else {
+                constexpr int q = m - NPV, jb = q / KK, kk = q % KK;
+                if constexpr (kk == 0) {
+                    const f32x16 zero = {};
+                    s_nxt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, f), __builtin_bit_cast(bf16x8, qf[kk]), zero, 0, 0, 0);
+                } else {
+                    s_nxt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, f), __builtin_bit_cast(bf16x8, qf[kk]), s_nxt[jb], 0, 0, 0);
+                }
+            }
+            // softmax slice of slot m
+            if constexpr (m < NMX) {
+                constexpr int jb = m >> 1, r0 = (m & 1) * 8;
+                float a0 = fmaxf(s_cur[jb][r0], s_cur[jb][r0 + 1]);
+                float a1 = fmaxf(s_cur[jb][r0 + 2], s_cur[jb][r0 + 3]);
+                a0 = fmaxf(a0, fmaxf(s_cur[jb][r0 + 4], s_cur[jb][r0 + 5]));
+                a1 = fmaxf(a1, fmaxf(s_cur[jb][r0 + 6], s_cur[jb][r0 + 7]));
+                mx[m] = fmaxf(a0, a1);
+            } else if constexpr (m == NMX) {
+                float mt = mx[0];
+#pragma unroll
+                for (int i = 1; i < NMX; ++i) mt = fmaxf(mt, mx[i]);
+                any = raise_max(row_max(mt) * c, alpha);
+            } else {
+                static_for<EPS>([&](auto xc) {
+                    constexpr int e = (m - NMX - 1) * EPS + decltype(xc)::value;
+                    if constexpr (e < NEX) exp_pair(s_cur, p_cur, e >> 2, e & 3);
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if (any) rescale_o(alpha);
+    };
+
+    // prologue: K_0 (and K_1), then S_0
+    copy_k(0, Kb(I0()));
+    if (ntiles > 1) copy_k(1, Kb(I1()));
+    sync_tiles();
+    qk(Kb(I0()), sA);
+
+    // iteration 0: softmax S_0 -> P_0 with S_1
+    {
+        sync_tiles();
+        if (ntiles > 2) copy_k(2, Kb(I0()));
+        copy_v(0, Vb(I0()));
+        float alpha;
+        softmax_max(sA, ntiles == 1 ? valid_last : kBn, alpha);
+        if (ntiles > 1) qk(Kb(I1()), sB);
+        softmax_exp(sA, pA);
+    }
+    // steady iterations t = 1 .. ntiles-2, unrolled by two so that every
+    // buffer and register set is fixed at compile time.
+    int t = 1;
+    for (; t + 2 < ntiles; t += 2) {
+        steady(t, I1());
+        steady(t + 1, I0());
+    }
+    if (t + 1 < ntiles) {
+        steady(t, I1());
+        ++t;
+    }
+    // last iteration t = ntiles-1 (>= 1): softmax of the last, possibly
+    // partial tile with PV_{t-1}; then PV of the last tile.
+    auto last = [&](auto par) {
+        constexpr int P = decltype(par)::value;  // t % 2
+        using IP = std::integral_constant<int, P>;
+        using IQ = std::integral_constant<int, 1 - P>;
+        f32x16 (&s_cur)[kNB] = P ? sB : sA;
+        u32x4 (&p_cur)[2 * kNB] = P ? pB : pA;
+        u32x4 (&p_prv)[2 * kNB] = P ? pA : pB;
+        sync_tiles();
+        copy_v(t, Vb(IP()));
+        float alpha;
+        const bool any = softmax_max(s_cur, valid_last, alpha);
+        pv(Vb(IQ()), p_prv);
+        softmax_exp(s_cur, p_cur);
+        if (any) rescale_o(alpha);
+        sync_tiles();
+        pv(Vb(IP()), p_cur);
+    };
+    if (ntiles == 1) {
+        sync_tiles();
+        pv(Vb(I0()), pA);
+    } else if (t & 1) {
+        last(I1());
+    } else {
+        last(I0());
     }
 
     // ---- epilogue: normalise and store this lane's half of its row straight
@@ -364,17 +579,27 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t *src, uint32_
     *(u32x4 *)dst = *(const u32x4 *)(src + (int64_t)c * 8);
 }
 
+// Waves per workgroup for a shape: 8 (one K/V tile per 256 query rows) when
+// that still gives at least half a workgroup per CU, else 4.
+int waves_for(int64_t B, int64_t S, int64_t Hl)
+{
+    const int64_t units8 = B * Hl * ((S + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave));
+    return units8 >= 128 ? 8 : 4;
+}
+
 }  // namespace
 
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl)
 {
-    return B * Hl * ((S + kBr - 1) / kBr);
+    const int nw = waves_for(B, S, Hl);
+    return B * Hl * ((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t B, int64_t S, int64_t Hl, int d, float scale,
                             const Placement &out, hipStream_t stream)
 {
+    const int nw = waves_for(B, S, Hl);
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -382,12 +607,13 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.out = out;
     a.S = S;
     a.Hl = (int32_t)Hl;
-    a.n_qtiles = (int32_t)((S + kBr - 1) / kBr);
+    a.n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
     a.n_units = (int32_t)attention_units(B, S, Hl);
     a.scale_log2 = scale * 1.4426950408889634f;
     void *args[] = {&a};
-    const void *fn = d == 128 ? (const void *)attn_fwd<128> : (const void *)attn_fwd<64>;
-    return hipLaunchKernel(fn, dim3(a.n_units), dim3(kThreads), args, 0, stream);
+    const void *fn = d == 128 ? (nw == 8 ? (const void *)attn_fwd<128, 8> : (const void *)attn_fwd<128, 4>)
+                              : (nw == 8 ? (const void *)attn_fwd<64, 8> : (const void *)attn_fwd<64, 4>);
+    return hipLaunchKernel(fn, dim3(a.n_units), dim3(64 * nw), args, 0, stream);
 }
 
 hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t Hl, int d,

@@ -13,7 +13,8 @@
  *
  * Attention is non-causal softmax(Q K^T * scale) V per head, no mask, no
  * dropout, computed with bf16 inputs, fp32 accumulation and bf16 output
- * (round to nearest even).
+ * (round to nearest even).  Inputs are expected to be finite: an Inf or NaN
+ * input gives unspecified values in the rows it reaches (never a fault).
  *
  * Layouts (bf16 = IEEE binary16-brain, passed as raw 16-bit patterns):
  *   Q, K, V, O_local : [B][S][Hl][d], contiguous, Hl = H / P.
