@@ -49,6 +49,8 @@ int check_limits(const ua_shape *shp, int P)
     const int64_t Hl = shp->H / P;
     const int64_t rows = shp->B * shp->S * Hl;
     if (rows >= (int64_t)1 << 31) return UA_ERR_UNSUPPORTED;
+    // row stride Hl*d: a 64-row K/V tile must span fewer than 2^31 bytes
+    if (Hl * shp->d > (int64_t)1 << 24) return UA_ERR_UNSUPPORTED;
     if (rows * (shp->d / 8) > (int64_t)UINT32_MAX) return UA_ERR_UNSUPPORTED;
     if (ua::attention_units(shp->B, shp->S, Hl) > INT32_MAX) return UA_ERR_UNSUPPORTED;
     return UA_OK;

@@ -219,24 +219,26 @@ void attn_fwd(AttnArgs a)
     // only these per-lane parts live in VGPRs.
     static_assert(GB == 4 * 1024, "four 1 KiB copies per column group");
     const int lrow = lane >> 2;
-    const int k_src = lrow * rs + ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
-    const int v_src = lrow * rs + (lane & 3) * 8;
-    // Keys past S (last, partial tile) read row S-1: finite data that the
-    // softmax masks out.
-    auto tile_copy = [&](const uint16_t *src, int lane_src, int64_t kv0, lds_u8 *dst) {
-        const uint16_t *base = src + kv0 * rs + lane_src;
-        const int last = (int)(S - 1 - kv0);  // last valid row of the tile
+    const unsigned k_chunk = (unsigned)((lane & 3) ^ ((lane >> 4) & 3)) * 16;  // bytes
+    const unsigned v_chunk = (unsigned)(lane & 3) * 16;
+    // Source address = wave-uniform base (scalar registers) + a non-negative
+    // 32-bit per-lane byte offset.  Rows past S (last, partial tile) are
+    // clamped to row S-1: finite data that the softmax masks out.
+    auto tile_copy = [&](const uint16_t *src, unsigned chunk, int64_t kv0, lds_u8 *dst) {
+        const char *base = (const char *)(src + kv0 * rs);
+        const bool full = kv0 + kBn <= S;
+        const int last = full ? kBn - 1 : (int)(S - 1 - kv0);  // last row inside S
 #pragma unroll
         for (int n = 0; n < NLD; ++n) {
             const int cp = wave * NLD + n;
-            const int row0 = 16 * (cp & 3);
-            const uint16_t *p = base + row0 * rs + (cp >> 2) * 32;
-            if (kv0 + kBn > S && row0 + lrow > last) p -= (row0 + lrow - last) * rs;
-            __builtin_amdgcn_global_load_lds((gbl_void *)p, (lds_void *)(dst + cp * 1024), 16, 0, 0);
+            const int row = 16 * (cp & 3) + lrow;
+            const int r = row < last ? row : last;
+            const unsigned off = (unsigned)(r * rs + (cp >> 2) * 32) * 2 + chunk;
+            __builtin_amdgcn_global_load_lds((gbl_void *)(base + off), (lds_void *)(dst + cp * 1024), 16, 0, 0);
         }
     };
-    auto copy_k = [&](int t, lds_u8 *dst) { tile_copy(kh, k_src, (int64_t)t * kBn, dst); };
-    auto copy_v = [&](int t, lds_u8 *dst) { tile_copy(vh, v_src, (int64_t)t * kBn, dst); };
+    auto copy_k = [&](int t, lds_u8 *dst) { tile_copy(kh, k_chunk, (int64_t)t * kBn, dst); };
+    auto copy_v = [&](int t, lds_u8 *dst) { tile_copy(vh, v_chunk, (int64_t)t * kBn, dst); };
     // All of this wave's copies have landed; after the barrier every wave's
     // have, and no wave still reads the buffers the next copies overwrite.
     auto sync_tiles = [&]() {
@@ -355,6 +357,10 @@ void attn_fwd(AttnArgs a)
         const bf16x2 hb = __builtin_convertvector(f, bf16x2);
         pb[cc][e2] = __builtin_bit_cast(unsigned, hb);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(hb, ones, l_run, false);
+        // Pin both results here in program order: otherwise the compiler
+        // sinks the whole exp work towards its first use (the next
+        // iteration's PV MFMAs) and runs it as one block without MFMA overlap.
+        asm volatile("" : "+v"(pb[cc][e2]), "+v"(l_run));
     };
     auto softmax_exp = [&](const f32x16 (&s)[kNB], u32x4 (&pb)[2 * kNB]) {
 #pragma unroll
@@ -467,6 +473,7 @@ void attn_fwd(AttnArgs a)
                 a0 = fmaxf(a0, fmaxf(s_cur[jb][r0 + 4], s_cur[jb][r0 + 5]));
                 a1 = fmaxf(a1, fmaxf(s_cur[jb][r0 + 6], s_cur[jb][r0 + 7]));
                 mx[m] = fmaxf(a0, a1);
+                asm volatile("" : "+v"(mx[m]));
             } else if constexpr (m == NMX) {
                 float mt = mx[0];
 #pragma unroll

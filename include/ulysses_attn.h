@@ -40,7 +40,9 @@
  * head dim, scale and launch-size limits (UA_ERR_UNSUPPORTED); then an empty
  * call (B == 0 or S == 0) returns UA_OK without touching any pointer;
  * otherwise NULL buffers (UA_ERR_NULL) and alignment (UA_ERR_ALIGN).  A
- * launch failure reported by the runtime gives UA_ERR_HIP.
+ * launch failure reported by the runtime gives UA_ERR_HIP.  Size limits
+ * (UA_ERR_UNSUPPORTED beyond them): B*S*Hl < 2^31 rows, B*S*Hl*d/8 < 2^32
+ * 16-byte chunks, Hl*d <= 2^24 elements per sequence row.
  */
 #ifndef ULYSSES_ATTN_H
 #define ULYSSES_ATTN_H

@@ -81,6 +81,9 @@ def test_attention_argument_validation(call):
     assert call(good, scale=float("nan")) == ua.UA_ERR_UNSUPPORTED
     assert call(good, scale=float("inf")) == ua.UA_ERR_UNSUPPORTED
     assert call((1, 1 << 30, 8, 128), P=1) == ua.UA_ERR_UNSUPPORTED  # beyond grid limits
+    assert call((1, 1, 1 << 18, 128), P=1) == ua.UA_ERR_UNSUPPORTED  # row stride Hl*d > 2^24
+    assert call((0, 1, 1 << 18, 128), P=1) == ua.UA_ERR_UNSUPPORTED  # limits come before "empty"
+    assert call((0, 1, 1 << 17, 128), P=1) == ua.UA_OK  # Hl*d = 2^24 is allowed
 
 
 @pytest.mark.parametrize("call", [_fused, _serial, _permute])
