@@ -11,9 +11,11 @@ starts.  Prints ONE JSON line:
   roofline  the fused attention kernel against the bf16 MFMA peak, from HIP
             events around every launch on the launch stream;
   detail    fused / serial (attention + separate permute) / attention-alone /
-            permute-alone times (medians over interleaved rounds), the
-            residual (fused - alone) / alone, the permute's HBM rate and the
-            fused epilogue's store volume;
+            permute-alone / store-only-epilogue times (medians over
+            interleaved rounds), the residual (fused - alone) / alone, the
+            permute's and the epilogue layout's HBM rates, and from one traced
+            fused call the per-work-unit epilogue store spans and the shader
+            clock the kernel ran at;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -52,6 +54,10 @@ def parse():
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--rounds", type=int, default=5,
                     help="interleaved rounds of fused / serial / alone / permute timing")
+    ap.add_argument("--cpu-all", action="store_true",
+                    help="instead of the benchmark: time the fp64 oracle on every workload "
+                         "(parity-check rows, and all rows where that takes under --full-limit s)")
+    ap.add_argument("--full-limit", type=float, default=120.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device-to-device copy of MIB MiB (a known-size "
                          "kernel for scaling HBM byte counters under rocprofv3 --pmc)")
@@ -117,23 +123,43 @@ def measured_traffic(launch_ms):
     return t.get("hbm_bytes_per_launch")
 
 
+def _oracle_sample(w, target_s, probe_dt_per_row):
+    """The rows the parity check uses for this workload, extended with further
+    distinct seeded rows until the sample is about target_s of oracle work."""
+    from ua_inputs import sampled_rows
+    rows = sampled_rows(dataclasses.replace(w, sampled=True))
+    want = int(target_s / max(probe_dt_per_row, 1e-9))
+    total = w.B * w.Hl * w.S
+    if want > len(rows):
+        rng = np.random.default_rng(w.seed + 2000)
+        seen = {tuple(r) for r in rows.tolist()}
+        extra = []
+        for flat in rng.permutation(total)[: min(total, 4 * want)]:
+            b, rem = divmod(int(flat), w.Hl * w.S)
+            h, srow = divmod(rem, w.S)
+            if (b, h, srow) not in seen:
+                extra.append((b, h, srow))
+                if len(rows) + len(extra) >= want:
+                    break
+        if extra:
+            rows = np.concatenate([rows, np.asarray(extra, dtype=np.int64)])
+    return rows[: max(want, 1)] if want < len(rows) else rows
+
+
 def cpu_baseline(w, Q, K, V, target_s):
     """The fp64 oracle as it stands, on the host cores, over a bounded sample of
     this workload's query rows (rows per second scaled to TFLOP/s)."""
     import oracle
-    from ua_inputs import sampled_rows
-    rows = sampled_rows(dataclasses.replace(w, sampled=True))
     scale = 1.0 / math.sqrt(w.d)
     threads = oracle.max_threads()
     flops_per_row = 4.0 * w.S * w.d
     # calibrate on a small batch, then time a sample sized for ~target_s
-    probe = rows[: max(threads, 8)]
+    from ua_inputs import sampled_rows
+    probe = sampled_rows(dataclasses.replace(w, sampled=True))[: max(4 * threads, 16)]
     t0 = time.perf_counter()
     oracle.attn_rows(Q, K, V, scale, probe)
-    dt = max(time.perf_counter() - t0, 1e-6)
-    n = int(min(len(rows), max(len(probe), len(probe) * target_s / dt)))
-    reps = max(1, int(math.ceil(n / len(rows))))
-    sample = np.concatenate([rows] * reps)[:n] if n > len(rows) else rows[:n]
+    dt_row = max(time.perf_counter() - t0, 1e-6) / len(probe)
+    sample = _oracle_sample(w, target_s, dt_row)
     t0 = time.perf_counter()
     oracle.attn_rows(Q, K, V, scale, sample)
     dt = time.perf_counter() - t0
@@ -142,13 +168,74 @@ def cpu_baseline(w, Q, K, V, target_s):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d query rows (of %d x %d) of the %s workload, full %d-key softmax each, fp64, %.1f s"
+        "sample": "%d query rows (of %d x %d; the parity-check rows first, then further seeded "
+                  "rows) of the %s workload, full %d-key softmax each, fp64, %.1f s"
                   % (len(sample), w.B * w.Hl, w.S, w.name, w.S, dt),
+        "rows_per_s": round(len(sample) / dt, 1),
+    }
+
+
+def cpu_all(full_limit_s: float) -> dict:
+    """Oracle timings on the host for every workload: the parity check's
+    sampled rows, and all rows where that fits full_limit_s (else the full
+    time extrapolated from the per-row time, and marked so)."""
+    import oracle
+    from ua_inputs import WORKLOADS, sampled_rows, workload_qkv
+    threads = oracle.max_threads()
+    res = []
+    for name, w in WORKLOADS.items():
+        Q, K, V = workload_qkv(w)
+        scale = 1.0 / math.sqrt(w.d)
+        rows = sampled_rows(dataclasses.replace(w, sampled=True))
+        t0 = time.perf_counter()
+        oracle.attn_rows(Q, K, V, scale, rows)
+        dt = time.perf_counter() - t0
+        per_row = dt / len(rows)
+        total_rows = w.B * w.Hl * w.S
+        est = per_row * total_rows
+        entry = {"workload": name, "check_rows": len(rows), "check_s": round(dt, 3),
+                 "rows_per_s": round(len(rows) / dt, 1),
+                 "gflops": round(4.0 * w.S * w.d * len(rows) / dt / 1e9, 2),
+                 "full_rows": total_rows}
+        if est <= full_limit_s:
+            t0 = time.perf_counter()
+            oracle.attn_all(Q, K, V, scale)
+            entry["full_s"] = round(time.perf_counter() - t0, 3)
+        else:
+            entry["full_s_extrapolated"] = round(est, 1)
+        res.append(entry)
+        print(json.dumps(entry), file=sys.stderr, flush=True)
+    return {"kind": "oracle", "cores": threads, "timings": res}
+
+
+def traced_call(ua, torch, q, k, v, w, dest) -> dict:
+    """One call of the measurement build: per-work-unit epilogue store spans
+    (from every wave's rows ready to every wave's stores complete) and the
+    shader clock (cycles over the 100 MHz constant clock)."""
+    n = ua.work_units(w.B, w.S, w.H, w.d, w.P)
+    trace = torch.zeros(4 * n, dtype=torch.int64, device=q.device)
+    ua.attn_ulysses_fused_trace(q, k, v, w.rank, w.P, dest, trace)
+    torch.cuda.synchronize()
+    t = trace.cpu().numpy().reshape(n, 4).astype(np.float64)
+    span_us = (t[:, 2] - t[:, 1]) / 100.0          # 100 MHz ticks -> us
+    life_us = (t[:, 2] - t[:, 0]) / 100.0
+    unit_bytes = w.out_bytes / n                    # mean bytes a work unit stores
+    ok = span_us > 0
+    return {
+        "trace_work_units": n,
+        "epilogue_span_us_mean": round(float(span_us.mean()), 3),
+        "epilogue_span_us_p90": round(float(np.percentile(span_us, 90)), 3),
+        "epilogue_unit_GBs_mean": round(float((unit_bytes / (span_us[ok] * 1e-6)).mean() / 1e9), 1) if ok.any() else None,
+        "epilogue_share_of_unit_time": round(float(span_us.sum() / life_us.sum()), 4),
+        "sclk_mhz_trace": round(float(t[:, 3].sum() / (life_us.sum() * 1e-6) / 1e6), 1),
     }
 
 
 def main():
     args = parse()
+    if args.cpu_all:
+        print(json.dumps(cpu_all(args.full_limit)), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path runs one Ulysses rank's share on "
               "one MI355X (the P ranks are P regions of its HBM); --gpus %d is not supported"
@@ -175,6 +262,8 @@ def main():
     fused = lambda: ua.attn_ulysses_fused(q, k, v, w.rank, w.P, dest)  # noqa: E731
     alone = lambda: ua.attn_serial(q, k, v, w.rank, w.P, o_local)       # noqa: E731
     perm = lambda: ua.a2a_permute(o_local, w.rank, w.P, dest)           # noqa: E731
+    scratch_dest = torch.empty_like(dest)
+    store_only = lambda: ua.epilogue_store_only(w.B, w.S, w.H, w.d, w.rank, w.P, scratch_dest)  # noqa: E731
 
     def serial():
         alone()
@@ -193,9 +282,10 @@ def main():
     # Baselines: fused, serial (attention + separate permute), attention
     # alone and permute alone, in interleaved rounds.
     reps = max(2, min(args.steps, int(200.0 / max(float(np.mean(per)), 1e-3)) + 1))
-    cmp = interleaved({"fused": fused, "serial": serial, "alone": alone, "perm": perm},
-                      args.rounds, reps)
+    cmp = interleaved({"fused": fused, "serial": serial, "alone": alone, "perm": perm,
+                       "store_only": store_only}, args.rounds, reps)
     per_serial, per_alone, per_perm = cmp["serial"], cmp["alone"], cmp["perm"]
+    tr = traced_call(ua, torch, q, k, v, w, scratch_dest)
 
     ms_step = total_ms / args.steps
     value = w.flops / (ms_step * 1e-3) / 1e12
@@ -235,6 +325,9 @@ def main():
             "hiding_ratio": round((t_s - t_f) / (t_s - t_a), 3) if t_s > t_a else None,
             "permute_hbm_GBs": round(2 * w.out_bytes / (t_p * 1e-3) / 1e9, 1),
             "epilogue_store_bytes": w.out_bytes,
+            "store_only_epilogue_ms_median": round(med(cmp["store_only"]), 4),
+            "store_only_epilogue_GBs": round(w.out_bytes / (med(cmp["store_only"]) * 1e-3) / 1e9, 1),
+            **tr,
             "wall_ms_timed_region": round(wall_ms, 3),
             "kernel_source_sha256_16": source_digest(),
         },

@@ -60,6 +60,12 @@ def lib() -> ctypes.CDLL:
     L.ua_local_bytes.restype = ctypes.c_size_t
     L.ua_version.argtypes = []
     L.ua_version.restype = i
+    L.attn_ulysses_fused_trace.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp, vp]
+    L.attn_ulysses_fused_trace.restype = i
+    L.ua_epilogue_store_only.argtypes = [i, i, vp, sp, vp]
+    L.ua_epilogue_store_only.restype = i
+    L.ua_work_units.argtypes = [sp, i]
+    L.ua_work_units.restype = ctypes.c_int64
     _lib = L
     return L
 
@@ -146,3 +152,35 @@ def a2a_permute(O_local, rank, P, out, stream=None):
                            _stream(stream))
     if st != UA_OK:
         raise UAError("a2a_permute", st)
+
+
+def work_units(B, S, H, d, P) -> int:
+    return int(lib().ua_work_units(ctypes.byref(Shape(B, S, H, d)), int(P)))
+
+
+def attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None):
+    """Measurement build of attn_ulysses_fused; ``trace`` is an int64 GPU tensor
+    of work_units(...) * 4 elements (see the C header for its contents)."""
+    import torch
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
+    n_units = int(lib().ua_work_units(ctypes.byref(shp), int(P)))
+    if trace.dtype != torch.int64 or not trace.is_cuda or not trace.is_contiguous() \
+            or trace.numel() != 4 * n_units:
+        raise TypeError("trace must be a contiguous int64 GPU tensor of %d elements" % (4 * n_units))
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_ulysses_fused_trace(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
+                                        ctypes.byref(shp), scale, _stream(stream), _ptr(trace))
+    if st != UA_OK:
+        raise UAError("attn_ulysses_fused_trace", st)
+
+
+def epilogue_store_only(B, S, H, d, rank, P, out, stream=None):
+    """The fused call's epilogue stores alone (closed-form values) into ``out``."""
+    shp = Shape(int(B), int(S), int(H), int(d))
+    _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
+    st = lib().ua_epilogue_store_only(int(rank), int(P), _ptr(out), ctypes.byref(shp), _stream(stream))
+    if st != UA_OK:
+        raise UAError("ua_epilogue_store_only", st)

@@ -81,7 +81,8 @@ ua::Placement local_placement(void *o_local, const ua_shape *shp, int P)
 }
 
 int attention_call(const void *Q, const void *K, const void *V, int rank, int P, void *out,
-                   const ua_shape *shp, float scale, void *stream, bool fused)
+                   const ua_shape *shp, float scale, void *stream, bool fused, uint64_t *trace = nullptr,
+                   bool want_trace = false)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);
@@ -89,12 +90,13 @@ int attention_call(const void *Q, const void *K, const void *V, int rank, int P,
     if (!isfinite(scale) || !(scale > 0.0f)) return UA_ERR_UNSUPPORTED;
     if ((st = check_limits(shp, P)) != UA_OK) return st;
     if (empty(shp)) return UA_OK;
-    if (!Q || !K || !V || !out) return UA_ERR_NULL;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return UA_ERR_ALIGN;
+    if (!Q || !K || !V || !out || (want_trace && !trace)) return UA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || (want_trace && !aligned16(trace)))
+        return UA_ERR_ALIGN;
     const ua::Placement o = fused ? dest_placement(out, shp, rank, P) : local_placement(out, shp, P);
     const hipError_t e = ua::launch_attention((const uint16_t *)Q, (const uint16_t *)K,
                                               (const uint16_t *)V, shp->B, shp->S, shp->H / P,
-                                              (int)shp->d, scale, o, (hipStream_t)stream);
+                                              (int)shp->d, scale, o, (hipStream_t)stream, trace);
     return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
@@ -112,6 +114,34 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P, vo
                 const ua_shape *shp, float scale, void *stream)
 {
     return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false);
+}
+
+int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                             const ua_shape *shp, float scale, void *stream, uint64_t *trace)
+{
+    return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, trace, true);
+}
+
+int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, void *stream)
+{
+    int64_t elems = 0;
+    int st = check_shape(shp, rank, P, &elems);
+    if (st != UA_OK) return st;
+    if ((st = check_limits(shp, P)) != UA_OK) return st;
+    if (empty(shp)) return UA_OK;
+    if (!out) return UA_ERR_NULL;
+    if (!aligned16(out)) return UA_ERR_ALIGN;
+    const hipError_t e = ua::launch_epilogue_only(shp->B, shp->S, shp->H / P, (int)shp->d,
+                                                  dest_placement(out, shp, rank, P), (hipStream_t)stream);
+    return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+int64_t ua_work_units(const ua_shape *shp, int P)
+{
+    int64_t elems = 0;
+    if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
+    if (empty(shp)) return 0;
+    return ua::attention_units(shp->B, shp->S, shp->H / P);
 }
 
 int a2a_permute(const void *O_local, int rank, int P, void *out, const ua_shape *shp, void *stream)

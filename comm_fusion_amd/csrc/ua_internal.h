@@ -23,10 +23,15 @@ struct Placement {
     int64_t head0;
 };
 
-// Attention over Hl local heads of [B][S][Hl][d] Q, K, V (bf16 bits).
+// Attention over Hl local heads of [B][S][Hl][d] Q, K, V (bf16 bits).  With
+// a non-null trace, the measurement build runs and fills 4 uint64 per unit.
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t B, int64_t S, int64_t Hl, int d, float scale,
-                            const Placement &out, hipStream_t stream);
+                            const Placement &out, hipStream_t stream, uint64_t *trace = nullptr);
+
+// The attention kernel's epilogue stores alone (closed-form values).
+hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
+                                hipStream_t stream);
 
 // Bit copy of O_local [B][S][Hl][d] rows into `out`.
 hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t Hl, int d,

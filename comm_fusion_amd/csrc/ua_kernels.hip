@@ -73,6 +73,7 @@ struct AttnArgs {
     int32_t n_qtiles;
     int32_t n_units;
     float scale_log2;  // softmax scale * log2(e)
+    uint64_t *trace;   // measurement build only: 4 timestamps per work unit
 };
 
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
@@ -156,10 +157,20 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
 // NW = 8: two waves per SIMD, one workgroup per CU.  NW = 4 only runs for
 // shapes with fewer work units than CUs, so it is built for one wave per SIMD
 // (and gets that SIMD's whole register file).
-template <int D, int NW>
+// TRACE: measurement build with the same arithmetic and output, which also
+// records per work unit (in a.trace[4*unit ..]): the 100 MHz constant clock
+// at the start, when every wave has its normalised rows ready (a workgroup
+// barrier), when every wave's epilogue stores have completed (vmcnt(0) and a
+// barrier), and the shader-clock cycles from start to end.
+template <int D, int NW, bool TRACE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd(AttnArgs a)
 {
+    uint64_t tr_t0 = 0, tr_c0 = 0;
+    if constexpr (TRACE) {
+        tr_t0 = __builtin_amdgcn_s_memrealtime();
+        tr_c0 = __builtin_amdgcn_s_memtime();
+    }
     constexpr int TILE = kBn * D * 2;        // bytes of one K (or V) tile
     constexpr int NLD = TILE / (NW * 1024);  // 1 KiB global->LDS copies per wave
     constexpr int KK = D / 16;               // MFMA k-steps over d for S^T
@@ -549,6 +560,11 @@ void attn_fwd(AttnArgs a)
     // into the destination slot (region p, row i, head g0 + h).
     const float lt = row_sum(l_run);
     const float inv = 1.0f / lt;
+    uint64_t tr_sb = 0;
+    if constexpr (TRACE) {
+        __syncthreads();
+        tr_sb = __builtin_amdgcn_s_memrealtime();
+    }
     if (s_q < S) {
         const Placement &o = a.out;
         const int64_t p = s_q / o.region_rows;
@@ -565,6 +581,55 @@ void attn_fwd(AttnArgs a)
                 *(u32x2 *)(dst + db * 32 + 8 * q4 + 4 * g) = w;
             }
     }
+    if constexpr (TRACE) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const uint64_t tr_se = __builtin_amdgcn_s_memrealtime();
+        const uint64_t tr_c1 = __builtin_amdgcn_s_memtime();
+        if (threadIdx.x == 0) {
+            uint64_t *t = a.trace + 4 * (int64_t)unit;
+            t[0] = tr_t0;
+            t[1] = tr_sb;
+            t[2] = tr_se;
+            t[3] = tr_c1 - tr_c0;
+        }
+    }
+}
+
+// Epilogue stores alone: the attention kernel's grid, work-unit order and
+// per-lane store pattern (8-byte chunks of one row per lane, placed by the
+// same Placement arithmetic), with a closed-form value instead of attention
+// output: element (s, head g, column c) gets bf16 bits (7s + 13g + 3c) & 0x3FFF
+// (finite, positive).  Measures what the destination layout sustains.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S, int32_t Hl, int32_t n_qtiles,
+                                                         int32_t n_units)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int il = lane & 31, g = lane >> 5;
+    const int unit = xcd_unit(blockIdx.x, n_units);
+    const int qt = unit % n_qtiles;
+    const int bh = unit / n_qtiles;
+    const int h = bh % Hl;
+    const int64_t b = bh / Hl;
+    const int64_t s_q = (int64_t)qt * (kRowsPerWave * NW) + wave * kRowsPerWave + il;
+    if (s_q >= S) return;
+    const int64_t p = s_q / o.region_rows;
+    const int64_t i = s_q - p * o.region_rows;
+    const int64_t gh = o.head0 + h;
+    uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + gh) * D;
+    const unsigned base = (unsigned)(7 * s_q + 13 * gh);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const unsigned c = db * 32 + 8 * q4 + 4 * g;
+            u32x2 w;
+            w[0] = ((base + 3 * c) & 0x3FFFu) | (((base + 3 * (c + 1)) & 0x3FFFu) << 16);
+            w[1] = ((base + 3 * (c + 2)) & 0x3FFFu) | (((base + 3 * (c + 3)) & 0x3FFFu) << 16);
+            *(u32x2 *)(dst + c) = w;
+        }
 }
 
 // Serial All-to-All: each thread copies one 16-byte chunk.  For a fixed
@@ -604,7 +669,7 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl)
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t B, int64_t S, int64_t Hl, int d, float scale,
-                            const Placement &out, hipStream_t stream)
+                            const Placement &out, hipStream_t stream, uint64_t *trace)
 {
     const int nw = waves_for(B, S, Hl);
     AttnArgs a;
@@ -617,10 +682,31 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
     a.n_units = (int32_t)attention_units(B, S, Hl);
     a.scale_log2 = scale * 1.4426950408889634f;
+    a.trace = trace;
     void *args[] = {&a};
-    const void *fn = d == 128 ? (nw == 8 ? (const void *)attn_fwd<128, 8> : (const void *)attn_fwd<128, 4>)
-                              : (nw == 8 ? (const void *)attn_fwd<64, 8> : (const void *)attn_fwd<64, 4>);
+    const void *fn;
+    if (trace)
+        fn = d == 128 ? (nw == 8 ? (const void *)attn_fwd<128, 8, true> : (const void *)attn_fwd<128, 4, true>)
+                      : (nw == 8 ? (const void *)attn_fwd<64, 8, true> : (const void *)attn_fwd<64, 4, true>);
+    else
+        fn = d == 128 ? (nw == 8 ? (const void *)attn_fwd<128, 8, false> : (const void *)attn_fwd<128, 4, false>)
+                      : (nw == 8 ? (const void *)attn_fwd<64, 8, false> : (const void *)attn_fwd<64, 4, false>);
     return hipLaunchKernel(fn, dim3(a.n_units), dim3(64 * nw), args, 0, stream);
+}
+
+hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
+                                hipStream_t stream)
+{
+    const int nw = waves_for(B, S, Hl);
+    Placement o = out;
+    int64_t S64 = S;
+    int32_t Hl32 = (int32_t)Hl;
+    int32_t n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
+    int32_t n_units = (int32_t)attention_units(B, S, Hl);
+    void *args[] = {&o, &S64, &Hl32, &n_qtiles, &n_units};
+    const void *fn = d == 128 ? (nw == 8 ? (const void *)epilogue_only<128, 8> : (const void *)epilogue_only<128, 4>)
+                              : (nw == 8 ? (const void *)epilogue_only<64, 8> : (const void *)epilogue_only<64, 4>);
+    return hipLaunchKernel(fn, dim3(n_units), dim3(64 * nw), args, 0, stream);
 }
 
 hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t Hl, int d,

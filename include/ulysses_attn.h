@@ -99,6 +99,38 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P,
 int a2a_permute(const void *O_local, int rank, int P, void *out,
                 const ua_shape *shp, void *stream);
 
+/*
+ * Measurement build of attn_ulysses_fused (the per-tile store spans the
+ * pages time for the piggybacked epilogue; review page, Fig. 7): the same
+ * arithmetic and bit-identical output, plus four uint64 per work unit in
+ * trace[4*u + 0..3], u in [0, ua_work_units):
+ *   [0] constant 100 MHz clock when the workgroup starts,
+ *   [1] the same clock once every wave of it has its normalised rows
+ *       (a workgroup barrier before the epilogue stores),
+ *   [2] the same clock once every wave's epilogue stores have completed,
+ *   [3] shader-clock cycles from [0] to [2] (so [3] / ([2]-[0]) * 100 MHz
+ *       is the clock the workgroup ran at).
+ * The two extra barriers make this build slightly slower than the product
+ * call.  trace: device buffer of ua_work_units(shp, P) * 4 uint64, 16-byte
+ * aligned, owned by the caller; NULL gives UA_ERR_NULL (for a non-empty call).
+ */
+int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int rank, int P,
+                             void *out, const ua_shape *shp, float scale, void *stream,
+                             uint64_t *trace);
+
+/*
+ * Epilogue stores alone, for measuring what the destination layout sustains:
+ * the fused call's grid, work-unit order and per-lane store pattern, writing
+ * a closed-form value instead of attention output.  Element (s, global head
+ * g, column c) of this rank's slots gets bf16 bits (7*s + 13*g + 3*c) & 0x3FFF;
+ * every other slot keeps its bytes.  Validation as a2a_permute.
+ */
+int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, void *stream);
+
+/* Work units (workgroups) of the attention launch for this shape; 0 for an
+ * invalid or empty shape. */
+int64_t ua_work_units(const ua_shape *shp, int P);
+
 /* Static English text for a status code; never NULL. */
 const char *ua_status_string(int status);
 

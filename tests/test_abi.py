@@ -109,3 +109,41 @@ def test_buffer_size_helpers():
     assert ua.local_bytes(1, 8, 5, 64, 2) == 0     # H % P != 0
     assert ua.dest_bytes(-1, 8, 4, 64) == 0
     assert ua.lib().ua_dest_bytes(None) == 0
+
+
+def _trace(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, trace=0x50000, scale=0.125):
+    return ua.lib().attn_ulysses_fused_trace(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale,
+                                             None, trace)
+
+
+def _store_only(shape, rank=0, P=2, out=O):
+    return ua.lib().ua_epilogue_store_only(rank, P, out, ctypes.byref(Shape(*shape)), None)
+
+
+def test_measurement_entry_points_validate_like_the_fused_call():
+    good = (1, 64, 4, 64)
+    assert _trace(good, trace=0) == ua.UA_ERR_NULL
+    assert _trace(good, trace=0x50008) == ua.UA_ERR_ALIGN
+    assert _trace(good, q=0) == ua.UA_ERR_NULL
+    assert _trace((1, 63, 4, 64)) == ua.UA_ERR_SHAPE
+    assert _trace(good, rank=2) == ua.UA_ERR_RANK
+    assert _trace(good, scale=0.0) == ua.UA_ERR_UNSUPPORTED
+    assert _trace((0, 64, 4, 64), q=0, k=0, v=0, out=0, trace=0) == ua.UA_OK
+    assert _store_only(good, out=0) == ua.UA_ERR_NULL
+    assert _store_only(good, out=O + 2) == ua.UA_ERR_ALIGN
+    assert _store_only((1, 64, 5, 64)) == ua.UA_ERR_SHAPE
+    assert _store_only(good, rank=-1) == ua.UA_ERR_RANK
+    assert _store_only((1, 64, 4, 96)) == ua.UA_ERR_UNSUPPORTED
+    assert _store_only((2, 0, 4, 64), out=0) == ua.UA_OK
+
+
+def test_work_units():
+    # 256-row units when that gives at least 128 of them, else 128-row units
+    assert ua.work_units(1, 65536, 40, 128, 8) == 5 * 256
+    assert ua.work_units(2, 32768, 24, 64, 4) == 2 * 6 * 128
+    assert ua.work_units(1, 16384, 24, 128, 8) == 3 * 64
+    assert ua.work_units(1, 4096, 24, 128, 8) == 3 * 32      # 3*16 < 128 -> 128-row units
+    assert ua.work_units(1, 512, 4, 64, 2) == 2 * 4
+    assert ua.work_units(3, 129, 9, 64, 3) == 3 * 3 * 2
+    assert ua.work_units(0, 64, 4, 64, 2) == 0
+    assert ua.work_units(1, 63, 4, 64, 2) == 0                 # invalid shape

@@ -73,6 +73,9 @@ SMALL = [
     (3, 130, 6, 2, 1, 64, 6),      # 130 = 2 Q tiles, 3 KV tiles (ragged)
     (1, 384, 3, 3, 2, 128, 7),     # regions of 128 rows, 3 full Q tiles
     (2, 96, 4, 4, 3, 128, 8),      # smaller than one Q tile
+    # enough work units for the 8-wave, 256-row workgroups, with ragged tails
+    (1, 520, 64, 1, 0, 128, 9),    # 520 = 2 full 256-row tiles + 8 rows; 8 KV tiles + 8 keys
+    (2, 1030, 32, 2, 1, 64, 10),   # d = 64, regions of 515 rows
 ]
 
 
