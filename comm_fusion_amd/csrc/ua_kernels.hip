@@ -235,21 +235,40 @@ void attn_fwd(AttnArgs a)
     // Source address = wave-uniform base (scalar registers) + a non-negative
     // 32-bit per-lane byte offset.  Rows past S (last, partial tile) are
     // clamped to row S-1: finite data that the softmax masks out.
-    auto tile_copy = [&](const uint16_t *src, unsigned chunk, int64_t kv0, lds_u8 *dst) {
-        const char *base = (const char *)(src + kv0 * rs);
-        const bool full = kv0 + kBn <= S;
-        const int last = full ? kBn - 1 : (int)(S - 1 - kv0);  // last row inside S
+    // (S < 2^31 rows, so tile arithmetic fits 32-bit scalar registers.)
+    const int S32 = (int)S;
+    // per-lane byte offsets of a full tile (the same for every tile)
+    unsigned koff[NLD], voff[NLD];
 #pragma unroll
-        for (int n = 0; n < NLD; ++n) {
-            const int cp = wave * NLD + n;
-            const int row = 16 * (cp & 3) + lrow;
-            const int r = row < last ? row : last;
-            const unsigned off = (unsigned)(r * rs + (cp >> 2) * 32) * 2 + chunk;
-            __builtin_amdgcn_global_load_lds((gbl_void *)(base + off), (lds_void *)(dst + cp * 1024), 16, 0, 0);
+    for (int n = 0; n < NLD; ++n) {
+        const int cp = wave * NLD + n;
+        const unsigned rowoff = (unsigned)((16 * (cp & 3) + lrow) * rs + (cp >> 2) * 32) * 2;
+        koff[n] = rowoff + k_chunk;
+        voff[n] = rowoff + v_chunk;
+    }
+    auto tile_copy = [&](const uint16_t *src, const unsigned *off, unsigned chunk, int t, lds_u8 *dst) {
+        const int kv0 = t * kBn;
+        const char *base = (const char *)(src + (int64_t)kv0 * rs);
+        if (kv0 + kBn <= S32) {
+#pragma unroll
+            for (int n = 0; n < NLD; ++n)
+                __builtin_amdgcn_global_load_lds((gbl_void *)(base + off[n]),
+                                                 (lds_void *)(dst + (wave * NLD + n) * 1024), 16, 0, 0);
+        } else {
+            asm volatile("");  // a real branch: full tiles keep their precomputed offsets
+            const int last = S32 - 1 - kv0;  // last row inside S
+#pragma unroll
+            for (int n = 0; n < NLD; ++n) {
+                const int cp = wave * NLD + n;
+                const int row = 16 * (cp & 3) + lrow;
+                const int r = row < last ? row : last;
+                const unsigned o = (unsigned)(r * rs + (cp >> 2) * 32) * 2 + chunk;
+                __builtin_amdgcn_global_load_lds((gbl_void *)(base + o), (lds_void *)(dst + cp * 1024), 16, 0, 0);
+            }
         }
     };
-    auto copy_k = [&](int t, lds_u8 *dst) { tile_copy(kh, k_chunk, (int64_t)t * kBn, dst); };
-    auto copy_v = [&](int t, lds_u8 *dst) { tile_copy(vh, v_chunk, (int64_t)t * kBn, dst); };
+    auto copy_k = [&](int t, lds_u8 *dst) { tile_copy(kh, koff, k_chunk, t, dst); };
+    auto copy_v = [&](int t, lds_u8 *dst) { tile_copy(vh, voff, v_chunk, t, dst); };
     // All of this wave's copies have landed; after the barrier every wave's
     // have, and no wave still reads the buffers the next copies overwrite.
     auto sync_tiles = [&]() {
@@ -478,18 +497,18 @@ void attn_fwd(AttnArgs a)
             }
             // softmax slice of slot m
             if constexpr (m < NMX) {
+                // one running max over the tile, two new values per v_max3
                 constexpr int jb = m >> 1, r0 = (m & 1) * 8;
-                float a0 = fmaxf(s_cur[jb][r0], s_cur[jb][r0 + 1]);
-                float a1 = fmaxf(s_cur[jb][r0 + 2], s_cur[jb][r0 + 3]);
-                a0 = fmaxf(a0, fmaxf(s_cur[jb][r0 + 4], s_cur[jb][r0 + 5]));
-                a1 = fmaxf(a1, fmaxf(s_cur[jb][r0 + 6], s_cur[jb][r0 + 7]));
-                mx[m] = fmaxf(a0, a1);
+                float r = m == 0 ? fmaxf(fmaxf(s_cur[jb][0], s_cur[jb][1]), s_cur[jb][2])
+                                 : fmaxf(fmaxf(mx[m - 1], s_cur[jb][r0]), s_cur[jb][r0 + 1]);
+                constexpr int i0 = m == 0 ? 3 : 2;
+#pragma unroll
+                for (int i = i0; i + 1 < 8; i += 2) r = fmaxf(fmaxf(r, s_cur[jb][r0 + i]), s_cur[jb][r0 + i + 1]);
+                if constexpr (i0 == 3) r = fmaxf(r, s_cur[jb][r0 + 7]);
+                mx[m] = r;
                 asm volatile("" : "+v"(mx[m]));
             } else if constexpr (m == NMX) {
-                float mt = mx[0];
-#pragma unroll
-                for (int i = 1; i < NMX; ++i) mt = fmaxf(mt, mx[i]);
-                any = raise_max(row_max(mt) * c, alpha);
+                any = raise_max(row_max(mx[NMX - 1]) * c, alpha);
             } else {
                 static_for<EPS>([&](auto xc) {
                     constexpr int e = (m - NMX - 1) * EPS + decltype(xc)::value;
