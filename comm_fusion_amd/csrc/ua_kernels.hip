@@ -499,8 +499,11 @@ void attn_fwd(AttnArgs a)
             if constexpr (m < NMX) {
                 // one running max over the tile, two new values per v_max3
                 constexpr int jb = m >> 1, r0 = (m & 1) * 8;
-                float r = m == 0 ? fmaxf(fmaxf(s_cur[jb][0], s_cur[jb][1]), s_cur[jb][2])
-                                 : fmaxf(fmaxf(mx[m - 1], s_cur[jb][r0]), s_cur[jb][r0 + 1]);
+                float r;
+                if constexpr (m == 0)
+                    r = fmaxf(fmaxf(s_cur[jb][0], s_cur[jb][1]), s_cur[jb][2]);
+                else
+                    r = fmaxf(fmaxf(mx[m - 1], s_cur[jb][r0]), s_cur[jb][r0 + 1]);
                 constexpr int i0 = m == 0 ? 3 : 2;
 #pragma unroll
                 for (int i = i0; i + 1 < 8; i += 2) r = fmaxf(fmaxf(r, s_cur[jb][r0 + i]), s_cur[jb][r0 + i + 1]);
