@@ -22,7 +22,9 @@
 //    O^T += V^T P^T; V^T comes from the key-major V tile through the gfx950
 //    transposing LDS read ds_read_b64_tr_b16;
 //  * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4
-//    (no VGPR staging), double buffered, one tile ahead;
+//    (no VGPR staging), through a ring of three buffers, one tile ahead;
+//    the operand reads of an iteration's first MFMAs are issued before its
+//    barrier, at the end of the previous iteration;
 //  * software pipeline: in steady state, iteration t interleaves the
 //    softmax of S_t with the MFMAs of O += V_{t-1} P_{t-1} and of S_{t+1},
 //    one MFMA plus a slice of softmax VALU work per issue slot, so every
@@ -104,14 +106,15 @@ __device__ __forceinline__ float row_sum(float x)
     return p[0] + p[1];
 }
 
-// MFMA operand reads from LDS in the steady-state loop, as explicit
-// instructions with compile-time offsets.  The compiler does not track them,
-// so it inserts no waits for them -- in particular none on the asynchronous
-// global->LDS copies into the other buffer, which it cannot tell apart from
-// these reads -- and each read is waited for exactly, with lgkm_wait, right
-// before the MFMA that consumes it.  No compiler-visible LDS or scalar-memory
-// operation is in flight while these are (every steady iteration ends with
-// all of them complete).
+// MFMA operand reads from LDS, as explicit instructions with compile-time
+// offsets (every LDS read of the attention kernel).  The compiler does not
+// track them, so it inserts no waits for them -- in particular none on the
+// asynchronous global->LDS copies into other buffers, which it cannot tell
+// apart from these reads -- and each read is waited for exactly, with
+// lgkm_wait, right before the MFMA that consumes it.  The kernel's scalar
+// loads all complete before its first LDS read, so the LDS counter counts
+// exactly these reads (the steady loop keeps a few in flight across
+// iterations).
 template <int OFF>
 __device__ __forceinline__ u32x4 lds_b128(unsigned addr)
 {
@@ -179,19 +182,12 @@ void attn_fwd(AttnArgs a)
     constexpr int BR = kRowsPerWave * NW;    // query rows per work unit
     static_assert(NLD >= 1 && TILE % (NW * 1024) == 0, "tile split");
 
-    // Two K and two V tiles as four distinct arrays, selected at compile
-    // time, so that the compiler-visible reads of one buffer (prologue and
-    // last iterations) never wait on the asynchronous writes into the other.
-    __shared__ __attribute__((aligned(1024))) unsigned char k0s[TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char k1s[TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char v0s[TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char v1s[TILE];
-    auto Kb = [&](auto j) -> lds_u8 * {
-        if constexpr (decltype(j)::value == 0) return (lds_u8 *)k0s; else return (lds_u8 *)k1s;
-    };
-    auto Vb = [&](auto j) -> lds_u8 * {
-        if constexpr (decltype(j)::value == 0) return (lds_u8 *)v0s; else return (lds_u8 *)v1s;
-    };
+    // Three K and three V tile buffers (a ring: tile j lives in buffer j % 3).
+    // Every LDS read in this kernel is an explicit instruction (lds_b128,
+    // lds_tr16) with exact waits, so the compiler needs no alias information
+    // about these arrays.
+    __shared__ __attribute__((aligned(1024))) unsigned char ks[3 * TILE];
+    __shared__ __attribute__((aligned(1024))) unsigned char vs[3 * TILE];
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
 
@@ -267,14 +263,12 @@ void attn_fwd(AttnArgs a)
             }
         }
     };
-    auto copy_k = [&](int t, lds_u8 *dst) { tile_copy(kh, koff, k_chunk, t, dst); };
-    auto copy_v = [&](int t, lds_u8 *dst) { tile_copy(vh, voff, v_chunk, t, dst); };
+    auto copy_k = [&](int t, int buf) { tile_copy(kh, koff, k_chunk, t, (lds_u8 *)ks + buf * TILE); };
+    auto copy_v = [&](int t, int buf) { tile_copy(vh, voff, v_chunk, t, (lds_u8 *)vs + buf * TILE); };
     // All of this wave's copies have landed; after the barrier every wave's
-    // have, and no wave still reads the buffers the next copies overwrite.
-    auto sync_tiles = [&]() {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
+    // have, and every wave has finished the previous iteration.  A plain
+    // s_barrier: reads still in flight (operand prefetch) target other buffers.
+    auto sync_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
 
     // This lane's query row; rows past S (ragged last Q tile) compute on row
     // S-1 and are not stored.
@@ -287,55 +281,65 @@ void attn_fwd(AttnArgs a)
     for (int kk = 0; kk < KK; ++kk)
         qf[kk] = *(const u32x4 *)(qh + s_ld * rs + 16 * kk + 8 * g);
 
-    // ---- S^T (64 keys x 32 queries) = K_t Q^T.  A operand: lane reads K row
-    // jb*32 + il, d-chunk 2kk+g (16 B).  Accumulator element r of block jb is
-    // key jb*32 + 8(r/4) + 4g + r%4 of the tile, query il.  (Prologue and
-    // first iteration; the steady loop issues the same products itself.)
-    auto qk = [&](const lds_u8 *kt, f32x16 (&s)[kNB]) {
-#pragma unroll
-        for (int jb = 0; jb < kNB; ++jb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[jb][r] = 0.f;
-            const int row = jb * 32 + il;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                const int sub = (2 * (kk & 1) + g) ^ ((row >> 2) & 3);
-                const u32x4 kf = *(const lds_u32x4 *)(kt + (kk >> 1) * GB + row * 64 + sub * 16);
-                s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                                __builtin_bit_cast(bf16x8, qf[kk]),
-                                                                s[jb], 0, 0, 0);
-            }
-        }
-    };
-
-    // ---- O^T (d x 32 queries) += V_t^T P_t^T, in 16-key chunks.
-    // B operand (P^T): chunk cc holds registers 8(cc%2)..+7 of block cc/2,
-    // i.e. element e is key 16cc + 8(e/4) + 4g + e%4.
-    // A operand (V^T): lane needs V[those keys][db*32 + lane%32]; two
-    // transposing reads, each giving 4 consecutive keys: in a 16-lane group,
-    // source lane i16 points at V row (k0 + i16/4), columns dd0 + 4(i16%4)
-    // .. +3 (dd0 = db*32 + 16*half), and result lane i16 gets column dd0+i16.
+    // Per-lane LDS byte addresses of the operand reads; buffers and blocks
+    // are instruction offsets.
+    //   K (A operand of S^T = K Q^T): row il of a 32-row block, 16 B chunk
+    //   (2*(kk%2) + g) ^ ((il/4)%4) of the 64 B group row.  Accumulator
+    //   element r of block jb is key jb*32 + 8(r/4) + 4g + r%4, query il.
+    //   V^T (A operand of O^T += V^T P^T), two transposing reads of 4 keys
+    //   each: in a 16-lane group, source lane i16 points at V row
+    //   k0 + i16/4, columns dd0 + 4(i16%4) .. +3 (dd0 = db*32 + 16*half),
+    //   and result lane i16 gets column dd0 + i16.  P^T (B operand): chunk
+    //   cc holds registers 8(cc%2)..+7 of score block cc/2, i.e. element e
+    //   is key 16cc + 8(e/4) + 4g + e%4.
+    const unsigned kb0 = (unsigned)(uintptr_t)(lds_u8 *)ks + il * 64 + (((0 + g) ^ ((il >> 2) & 3)) * 16);
+    const unsigned kb1 = (unsigned)(uintptr_t)(lds_u8 *)ks + il * 64 + (((2 + g) ^ ((il >> 2) & 3)) * 16);
+    const unsigned vb = (unsigned)(uintptr_t)(lds_u8 *)vs + (4 * g + (i16 >> 2)) * 64 + (16 * half + 4 * (i16 & 3)) * 2;
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    const int v_lane = (4 * g + (i16 >> 2)) * 64 + (16 * half + 4 * (i16 & 3)) * 2;
-    auto pv = [&](const lds_u8 *vt, const u32x4 (&pb)[2 * kNB]) {
-#pragma unroll
-        for (int cc = 0; cc < 2 * kNB; ++cc)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const lds_u8 *p1 = vt + db * GB + 16 * cc * 64 + v_lane;
-                const u32x2 a1 = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)p1));
-                const u32x2 a2 = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p1 + 8 * 64)));
-                const u32x4 af = {a1[0], a1[1], a2[0], a2[1]};
+    // S^T of the K tile in buffer kbuf (outside the steady loop).
+    auto qk = [&](int kbuf, f32x16 (&s)[kNB]) {
+        const unsigned ko = kbuf * TILE;
+        static_for<kNB>([&](auto jc) {
+            constexpr int jb = decltype(jc)::value;
+            u32x4 kf[KK];
+            static_for<KK>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                kf[kk] = lds_b128<(kk >> 1) * GB + jb * 32 * 64>(((kk & 1) ? kb1 : kb0) + ko);
+            });
+            const f32x16 zero = {};
+            s[jb] = zero;
+            static_for<KK>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                lgkm_wait<KK - 1 - kk>(kf[kk]);
+                s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]),
+                                                                __builtin_bit_cast(bf16x8, qf[kk]), s[jb], 0, 0, 0);
+            });
+        });
+    };
+    // O^T += V^T P^T for the V tile in buffer vbuf (outside the steady loop).
+    auto pv = [&](int vbuf, const u32x4 (&pb)[2 * kNB]) {
+        const unsigned vo = vbuf * TILE;
+        static_for<2 * kNB>([&](auto ccc) {
+            constexpr int cc = decltype(ccc)::value;
+            u32x4 af[DB];
+            static_for<DB>([&](auto dbc) {
+                constexpr int db = decltype(dbc)::value;
+                constexpr int off = db * GB + 16 * cc * 64;
+                const u32x2 a1 = lds_tr16<off>(vb + vo);
+                const u32x2 a2 = lds_tr16<off + 8 * 64>(vb + vo);
+                af[db] = u32x4{a1[0], a1[1], a2[0], a2[1]};
+            });
+            static_for<DB>([&](auto dbc) {
+                constexpr int db = decltype(dbc)::value;
+                lgkm_wait<2 * (DB - 1 - db)>(af[db]);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, af), __builtin_bit_cast(bf16x8, pb[cc]), oacc[db],
-                    0, 0, 0);
-            }
+                    __builtin_bit_cast(bf16x8, af[db]), __builtin_bit_cast(bf16x8, pb[cc]), oacc[db], 0, 0, 0);
+            });
+        });
     };
 
     // ---- online softmax in the log2 domain.  m_run is the running max of
@@ -407,19 +411,25 @@ void attn_fwd(AttnArgs a)
     };
 
     // ---- software pipeline over KV tiles.  Iteration t: softmax of S_t
-    // interleaves with the MFMAs of PV_{t-1} and of S_{t+1}; tile copies run
-    // one iteration ahead (K_{t+2} and V_t are copied during iteration t).
-    // K_j and V_j live in buffer j % 2.
+    // interleaves with the MFMAs of PV_{t-1} and of S_{t+1}.  Tile copies
+    // run one iteration ahead through a three-buffer ring (iteration t
+    // copies K_{t+3} and V_{t+1}), so the operand reads of the next
+    // iteration's first MFMAs can be issued before its barrier.
     const int ntiles = (int)((S + kBn - 1) / kBn);
     const int valid_last = (int)(S - (int64_t)(ntiles - 1) * kBn);
-    f32x16 sA[kNB], sB[kNB];         // S of even / odd tiles
-    u32x4 pA[2 * kNB], pB[2 * kNB];  // packed P of even / odd tiles
+    f32x16 s_cur[kNB], s_nxt[kNB];         // S_t, S_{t+1}
+    u32x4 p_cur[2 * kNB], p_prv[2 * kNB];  // packed P_t, P_{t-1}
+    auto rotate = [&]() {
+#pragma unroll
+        for (int jb = 0; jb < kNB; ++jb) s_cur[jb] = s_nxt[jb];
+#pragma unroll
+        for (int cc = 0; cc < 2 * kNB; ++cc) p_prv[cc] = p_cur[cc];
+    };
 
     // Steady iteration with an explicit issue order.  Slot m issues the LDS
-    // reads for MFMA m + kPF, MFMA m, and a fixed slice of the softmax VALU
-    // work; scheduling fences keep the compiler from gathering the VALU work
-    // into one block (a wave whose MFMAs run back to back while its VALU
-    // work sits in one block leaves the matrix pipe idle during that block).
+    // reads for MFMA m + kPF (of the next iteration near the end), MFMA m,
+    // and a fixed slice of the softmax VALU work; scheduling fences keep
+    // the compiler from gathering the VALU work into one block.
     //   MFMA order: PV_{t-1} (chunk cc, block db), then S_{t+1} (block jb,
     //   k-step kk).  VALU order: tile max of S_t in NMX slots, then the
     //   raise step, then EPS exp pairs per slot.
@@ -430,55 +440,58 @@ void attn_fwd(AttnArgs a)
     constexpr int NEX = 8 * kNB;  // exp pairs
     constexpr int EPS = (NEX + (NM - NMX - 1) - 1) / (NM - NMX - 1);
     static_assert(NM > NMX + 1, "no slots left for the exp pairs");
-    // Per-lane LDS byte offsets of the steady-state operand reads: K row il
-    // of a 32-row block, 16 B chunk (2*(kk%2) + g) ^ ((il/4)%4); the rest of
-    // each address is a compile-time offset plus the buffer base.
-    const unsigned k_lane0 = il * 64 + (((0 + g) ^ ((il >> 2) & 3)) * 16);
-    const unsigned k_lane1 = il * 64 + (((2 + g) ^ ((il >> 2) & 3)) * 16);
+    static_assert(kPF <= NPV, "the prefetch crossing into the next iteration reads V fragments");
     constexpr int NRD_PV = 2, NRD_S = 1;  // LDS reads per MFMA fragment
-    // reads issued after fragment m's and before MFMA m (fragments m+1 .. m+kPF)
+    // reads issued after fragment m's and before MFMA m (fragments m+1 .. m+kPF,
+    // those past NM belonging to the next iteration)
     auto after = [](int m) constexpr {
         int n = 0;
-        for (int j = m + 1; j <= m + kPF && j < NM; ++j) n += j < NPV ? NRD_PV : NRD_S;
+        for (int j = m + 1; j <= m + kPF; ++j) n += (j % NM) < NPV ? NRD_PV : NRD_S;
         return n;
     };
-    auto load_frag = [&](auto mc, u32x4 &dst, unsigned vbase, unsigned kbase) {
+    // fragment m of an iteration whose V_{t-1} / K_{t+1} sit in buffers VBUF / KBUF
+    auto load_frag = [&](auto mc, auto vbufc, auto kbufc, u32x4 &dst) {
         constexpr int m = decltype(mc)::value;
+        constexpr int VO = decltype(vbufc)::value * TILE, KO = decltype(kbufc)::value * TILE;
         if constexpr (m < NPV) {
             constexpr int cc = m / DB, db = m % DB;
-            constexpr int off = db * GB + 16 * cc * 64;
-            const u32x2 a1 = lds_tr16<off>(vbase + v_lane);
-            const u32x2 a2 = lds_tr16<off + 8 * 64>(vbase + v_lane);
+            constexpr int off = VO + db * GB + 16 * cc * 64;
+            const u32x2 a1 = lds_tr16<off>(vb);
+            const u32x2 a2 = lds_tr16<off + 8 * 64>(vb);
             dst = u32x4{a1[0], a1[1], a2[0], a2[1]};
         } else {
             constexpr int q = m - NPV, jb = q / KK, kk = q % KK;
-            constexpr int off = (kk >> 1) * GB + jb * 32 * 64;
-            dst = lds_b128<off>(kbase + ((kk & 1) ? k_lane1 : k_lane0));
+            constexpr int off = KO + (kk >> 1) * GB + jb * 32 * 64;
+            dst = lds_b128<off>((kk & 1) ? kb1 : kb0);
         }
     };
+    // Operand fragments in flight, carried across iterations: fragment m of
+    // every iteration sits in fr[m % FR], so the ring size must divide NM.
+    constexpr int FR = 4;
+    static_assert(FR > kPF && NM % FR == 0, "fragment ring");
+    u32x4 fr[FR];
     auto steady = [&](int t, auto par) {
-        constexpr int P = decltype(par)::value;  // t % 2
-        using IP = std::integral_constant<int, P>;
-        using IQ = std::integral_constant<int, 1 - P>;
-        f32x16 (&s_cur)[kNB] = P ? sB : sA;
-        f32x16 (&s_nxt)[kNB] = P ? sA : sB;
-        u32x4 (&p_cur)[2 * kNB] = P ? pB : pA;
-        u32x4 (&p_prv)[2 * kNB] = P ? pA : pB;
-        const unsigned vbase = (unsigned)(uintptr_t)Vb(IQ());
-        const unsigned kbase = (unsigned)(uintptr_t)Kb(IQ());
+        constexpr int P = decltype(par)::value;  // t % 3
+        using VB = std::integral_constant<int, (P + 2) % 3>;   // V_{t-1}
+        using KB = std::integral_constant<int, (P + 1) % 3>;   // K_{t+1}
+        using VBn = std::integral_constant<int, P>;            // V_t: next iteration
+        using KBn = std::integral_constant<int, (P + 2) % 3>;  // K_{t+2}: next iteration
+        // K_{t+2} and V_t (copied during iteration t-1) have landed and
+        // every wave is done with iteration t-1: K_t's and V_{t-2}'s buffers
+        // are free for K_{t+3} and V_{t+1}.
         sync_tiles();
-        if (t + 2 < ntiles) copy_k(t + 2, Kb(IP()));
-        copy_v(t, Vb(IP()));
-        u32x4 fr[kPF + 1];
-        static_for<kPF>([&](auto mc) { load_frag(mc, fr[decltype(mc)::value], vbase, kbase); });
+        if (t + 3 < ntiles) copy_k(t + 3, P);
+        copy_v(t + 1, (P + 1) % 3);
         float mx[NMX];
         float alpha = 1.f;
         bool any = false;
         static_for<NM>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             if constexpr (m + kPF < NM)
-                load_frag(std::integral_constant<int, m + kPF>(), fr[(m + kPF) % (kPF + 1)], vbase, kbase);
-            u32x4 f = fr[m % (kPF + 1)];
+                load_frag(std::integral_constant<int, m + kPF>(), VB(), KB(), fr[(m + kPF) % FR]);
+            else
+                load_frag(std::integral_constant<int, m + kPF - NM>(), VBn(), KBn(), fr[(m + kPF - NM) % FR]);
+            u32x4 f = fr[m % FR];
             lgkm_wait<after(m)>(f);
             if constexpr (m < NPV) {
                 constexpr int cc = m / DB, db = m % DB;
@@ -521,61 +534,68 @@ void attn_fwd(AttnArgs a)
             __builtin_amdgcn_sched_barrier(0);
         });
         if (any) rescale_o(alpha);
+        rotate();
+    };
+    // Full wait (also drains operand reads still in flight) and barrier.
+    auto sync_all = [&]() {
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
     };
 
-    // prologue: K_0 (and K_1), then S_0
-    copy_k(0, Kb(I0()));
-    if (ntiles > 1) copy_k(1, Kb(I1()));
-    sync_tiles();
-    qk(Kb(I0()), sA);
+    // prologue: K_0, K_1, K_2 and V_0, then S_0
+    copy_k(0, 0);
+    if (ntiles > 1) copy_k(1, 1);
+    if (ntiles > 2) copy_k(2, 2);
+    copy_v(0, 0);
+    sync_all();
+    qk(0, s_cur);
 
     // iteration 0: softmax S_0 -> P_0 with S_1
-    {
-        sync_tiles();
-        if (ntiles > 2) copy_k(2, Kb(I0()));
-        copy_v(0, Vb(I0()));
-        float alpha;
-        softmax_max(sA, ntiles == 1 ? valid_last : kBn, alpha);
-        if (ntiles > 1) qk(Kb(I1()), sB);
-        softmax_exp(sA, pA);
-    }
-    // steady iterations t = 1 .. ntiles-2, unrolled by two so that every
-    // buffer and register set is fixed at compile time.
-    int t = 1;
-    for (; t + 2 < ntiles; t += 2) {
-        steady(t, I1());
-        steady(t + 1, I0());
-    }
-    if (t + 1 < ntiles) {
-        steady(t, I1());
-        ++t;
-    }
-    // last iteration t = ntiles-1 (>= 1): softmax of the last, possibly
-    // partial tile with PV_{t-1}; then PV of the last tile.
-    auto last = [&](auto par) {
-        constexpr int P = decltype(par)::value;  // t % 2
-        using IP = std::integral_constant<int, P>;
-        using IQ = std::integral_constant<int, 1 - P>;
-        f32x16 (&s_cur)[kNB] = P ? sB : sA;
-        u32x4 (&p_cur)[2 * kNB] = P ? pB : pA;
-        u32x4 (&p_prv)[2 * kNB] = P ? pA : pB;
-        sync_tiles();
-        copy_v(t, Vb(IP()));
+    float alpha0;
+    softmax_max(s_cur, ntiles == 1 ? valid_last : kBn, alpha0);
+    if (ntiles == 1) {
+        softmax_exp(s_cur, p_cur);
+        pv(0, p_cur);
+    } else {
+        qk(1, s_nxt);
+        softmax_exp(s_cur, p_cur);
+        rotate();
+        // every wave is done with K_0: its buffer takes K_3; V_1 goes to buffer 1
+        sync_all();
+        if (ntiles > 3) copy_k(3, 0);
+        copy_v(1, 1);
+        // operands of the first steady iteration (V_0 and K_2, landed)
+        if (ntiles > 2)
+            static_for<kPF>([&](auto mc) {
+                load_frag(mc, std::integral_constant<int, 0>(), std::integral_constant<int, 2>(),
+                          fr[decltype(mc)::value % FR]);
+            });
+        // steady iterations t = 1 .. ntiles-2, unrolled by three so that
+        // every buffer is fixed at compile time.
+        using I2 = std::integral_constant<int, 2>;
+        int t = 1;
+        for (; t + 3 < ntiles; t += 3) {
+            steady(t, I1());
+            steady(t + 1, I2());
+            steady(t + 2, I0());
+        }
+        if (t + 1 < ntiles) {
+            steady(t, I1());
+            ++t;
+        }
+        if (t + 1 < ntiles) {
+            steady(t, I2());
+            ++t;
+        }
+        // last iteration t = ntiles-1: softmax of the last, possibly partial
+        // tile with PV_{t-1}; then PV of the last tile.  No copies left.
+        sync_all();
         float alpha;
         const bool any = softmax_max(s_cur, valid_last, alpha);
-        pv(Vb(IQ()), p_prv);
+        pv((t + 2) % 3, p_prv);
         softmax_exp(s_cur, p_cur);
         if (any) rescale_o(alpha);
-        sync_tiles();
-        pv(Vb(IP()), p_cur);
-    };
-    if (ntiles == 1) {
-        sync_tiles();
-        pv(Vb(I0()), pA);
-    } else if (t & 1) {
-        last(I1());
-    } else {
-        last(I0());
+        pv(t % 3, p_cur);
     }
 
     // ---- epilogue: normalise and store this lane's half of its row straight
