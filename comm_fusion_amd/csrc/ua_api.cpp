@@ -52,7 +52,7 @@ int check_limits(const ua_shape *shp, int P)
     // row stride Hl*d: a 64-row K/V tile must span fewer than 2^31 bytes
     if (Hl * shp->d > (int64_t)1 << 24) return UA_ERR_UNSUPPORTED;
     if (rows * (shp->d / 8) > (int64_t)UINT32_MAX) return UA_ERR_UNSUPPORTED;
-    if (ua::attention_units(shp->B, shp->S, Hl) > INT32_MAX) return UA_ERR_UNSUPPORTED;
+    if (ua::attention_units(shp->B, shp->S, Hl, (int)shp->d) > INT32_MAX) return UA_ERR_UNSUPPORTED;
     return UA_OK;
 }
 
@@ -141,7 +141,7 @@ int64_t ua_work_units(const ua_shape *shp, int P)
     int64_t elems = 0;
     if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
     if (empty(shp)) return 0;
-    return ua::attention_units(shp->B, shp->S, shp->H / P);
+    return ua::attention_units(shp->B, shp->S, shp->H / P, (int)shp->d);
 }
 
 int a2a_permute(const void *O_local, int rank, int P, void *out, const ua_shape *shp, void *stream)

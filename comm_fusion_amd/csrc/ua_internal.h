@@ -38,6 +38,6 @@ hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t
                           const Placement &out, hipStream_t stream);
 
 // Work units (one workgroup each) the attention launch uses for this shape.
-int64_t attention_units(int64_t B, int64_t S, int64_t Hl);
+int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);
 
 }  // namespace ua

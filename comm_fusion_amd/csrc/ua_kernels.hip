@@ -695,17 +695,18 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t *src, uint32_
 
 // Waves per workgroup for a shape: 8 (one K/V tile per 256 query rows) when
 // that still gives at least half a workgroup per CU, else 4.
-int waves_for(int64_t B, int64_t S, int64_t Hl)
+int waves_for(int64_t B, int64_t S, int64_t Hl, int d)
 {
+    (void)d;
     const int64_t units8 = B * Hl * ((S + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave));
     return units8 >= 128 ? 8 : 4;
 }
 
 }  // namespace
 
-int64_t attention_units(int64_t B, int64_t S, int64_t Hl)
+int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const int nw = waves_for(B, S, Hl);
+    const int nw = waves_for(B, S, Hl, d);
     return B * Hl * ((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
 }
 
@@ -713,7 +714,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             int64_t B, int64_t S, int64_t Hl, int d, float scale,
                             const Placement &out, hipStream_t stream, uint64_t *trace)
 {
-    const int nw = waves_for(B, S, Hl);
+    const int nw = waves_for(B, S, Hl, d);
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -722,7 +723,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.S = S;
     a.Hl = (int32_t)Hl;
     a.n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
-    a.n_units = (int32_t)attention_units(B, S, Hl);
+    a.n_units = (int32_t)attention_units(B, S, Hl, d);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.trace = trace;
     void *args[] = {&a};
@@ -739,12 +740,12 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
                                 hipStream_t stream)
 {
-    const int nw = waves_for(B, S, Hl);
+    const int nw = waves_for(B, S, Hl, d);
     Placement o = out;
     int64_t S64 = S;
     int32_t Hl32 = (int32_t)Hl;
     int32_t n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
-    int32_t n_units = (int32_t)attention_units(B, S, Hl);
+    int32_t n_units = (int32_t)attention_units(B, S, Hl, d);
     void *args[] = {&o, &S64, &Hl32, &n_qtiles, &n_units};
     const void *fn = d == 128 ? (nw == 8 ? (const void *)epilogue_only<128, 8> : (const void *)epilogue_only<128, 4>)
                               : (nw == 8 ? (const void *)epilogue_only<64, 8> : (const void *)epilogue_only<64, 4>);
