@@ -328,6 +328,9 @@ def main():
             "store_only_epilogue_ms_median": round(med(cmp["store_only"]), 4),
             "store_only_epilogue_GBs": round(w.out_bytes / (med(cmp["store_only"]) * 1e-3) / 1e9, 1),
             **tr,
+            # the same against the peak scaled to the clock the traced call ran at
+            "pct_bf16_peak_at_traced_clock": round(100.0 * value / (PEAK_BF16_TFLOPS * tr["sclk_mhz_trace"] / 2400.0), 2)
+            if tr.get("sclk_mhz_trace") else None,
             "wall_ms_timed_region": round(wall_ms, 3),
             "kernel_source_sha256_16": source_digest(),
         },

@@ -110,7 +110,7 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
  *   [2] the same clock once every wave's epilogue stores have completed,
  *   [3] shader-clock cycles from [0] to [2] (so [3] / ([2]-[0]) * 100 MHz
  *       is the clock the workgroup ran at).
- * The two extra barriers make this build slightly slower than the product
+ * The two extra barriers make the measurement build slightly slower than the product
  * call.  trace: device buffer of ua_work_units(shp, P) * 4 uint64, 16-byte
  * aligned, owned by the caller; NULL gives UA_ERR_NULL (for a non-empty call).
  */

@@ -178,6 +178,18 @@ def test_scale_is_applied():
         _compare_rows(dest, Q, K, V, rows, 2, 2, 0, scale, "scale %g" % scale)
 
 
+def test_wide_rows_many_heads():
+    # 512 local heads of d = 128: a sequence row spans 128 KiB, so the tile-copy
+    # offsets reach 63 rows x 128 KiB; ragged S on the 8-wave path.
+    B, S, H, P, rank, d = 1, 70, 1024, 2, 1, 128
+    Q, K, V = _case(B, S, H, P, rank, d, 11)
+    scale = 1.0 / math.sqrt(d)
+    dest = _fused(Q, K, V, rank, P, H)
+    check_dest_layout(dest, B, S, H, d, P, rank)
+    rows = sampled_rows(Workload("t", B, S, H, P, rank, d, 11, sampled=True), n_per_head=8)
+    _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, "wide rows")
+
+
 @pytest.mark.parametrize("name", ["dit_image", "dit_long", "video_dit", "mixed"])
 def test_workloads_at_full_size(name):
     # The configurations the benchmark times, at full size: sampled rows
