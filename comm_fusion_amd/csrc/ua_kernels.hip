@@ -468,8 +468,8 @@ void attn_fwd(AttnArgs a)
     // Operand fragments in flight, carried across iterations: fragment m of
     // every iteration sits in fr[m % FR], so the ring size must divide NM.
     constexpr int FR = 4;
-    static_assert(FR > kPF && NM % FR == 0, "fragment ring");
-    u32x4 fr[FR];
+    static_assert(FR > kPF && NM % FR == 0 && FR == 4, "fragment ring");
+    u32x4 fr[FR] = {};
     auto steady = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;  // t % 3
         using VB = std::integral_constant<int, (P + 2) % 3>;   // V_{t-1}
@@ -491,7 +491,7 @@ void attn_fwd(AttnArgs a)
                 load_frag(std::integral_constant<int, m + kPF>(), VB(), KB(), fr[(m + kPF) % FR]);
             else
                 load_frag(std::integral_constant<int, m + kPF - NM>(), VBn(), KBn(), fr[(m + kPF - NM) % FR]);
-            u32x4 f = fr[m % FR];
+            u32x4 &f = fr[m % FR];
             lgkm_wait<after(m)>(f);
             if constexpr (m < NPV) {
                 constexpr int cc = m / DB, db = m % DB;
@@ -589,6 +589,10 @@ void attn_fwd(AttnArgs a)
         }
         // last iteration t = ntiles-1: softmax of the last, possibly partial
         // tile with PV_{t-1}; then PV of the last tile.  No copies left.
+        // The last steady iteration prefetched fragments for an iteration
+        // that does not come: their reads are still in flight, so their
+        // registers stay reserved (tied to this wait) until they land.
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fr[0]), "+v"(fr[1]), "+v"(fr[2]), "+v"(fr[3])::"memory");
         sync_all();
         float alpha;
         const bool any = softmax_max(s_cur, valid_last, alpha);

@@ -190,6 +190,31 @@ def test_wide_rows_many_heads():
     _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, "wide rows")
 
 
+@pytest.mark.parametrize("H,d", [(64, 128), (4, 64)])  # P = 2: 8-wave and 4-wave launches
+@pytest.mark.parametrize("pattern", ["rising", "spikes"])
+def test_running_max_rises_and_jumps(H, d, pattern):
+    # Scores whose running max keeps rising along the keys (K rows scaled by
+    # 0.25 .. 3.25), or jumps far past it in the middle of the sequence (three
+    # keys scaled by 60: against the earlier max, exp of such a score
+    # overflows fp32 for a few percent of the rows).  The online softmax has to
+    # raise its max and rescale in the middle KV tiles, not only at the ends.
+    from ua_inputs import to_bf16_bits
+    B, S, P, rank = 1, 1030, 2, 1
+    Q, K, V = _case(B, S, H, P, rank, d, 12)
+    Kf = bits_to_f64(K)
+    if pattern == "rising":
+        Kf *= (0.25 + 3.0 * np.arange(S) / S)[None, :, None, None]
+    else:
+        for j in (200, 611, 777):
+            Kf[:, j] *= 60.0
+    K = to_bf16_bits(Kf.astype(np.float32))
+    scale = 1.0 / math.sqrt(d)
+    dest = _fused(Q, K, V, rank, P, H)
+    check_dest_layout(dest, B, S, H, d, P, rank)
+    rows = sampled_rows(Workload("t", B, S, H, P, rank, d, 12, sampled=True), n_per_head=96)
+    _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, pattern)
+
+
 @pytest.mark.parametrize("name", ["dit_image", "dit_long", "video_dit", "mixed"])
 def test_workloads_at_full_size(name):
     # The configurations the benchmark times, at full size: sampled rows

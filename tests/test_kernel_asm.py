@@ -1,0 +1,195 @@
+"""Static checks on the gfx950 assembly of the attention kernels (no GPU).
+
+The kernels issue their LDS operand reads as inline assembly and wait for
+them with explicit ``s_waitcnt lgkmcnt(N)``; the compiler treats such a
+read's destination registers as written when the instruction is issued.  If
+it copies or spills one of them before the wait (register pressure), the
+copy takes the register's old contents.  These tests compile the kernels and
+check that this cannot happen: no register spills or scratch use, and no
+instruction touches a register of a read still in flight.
+"""
+import re
+
+import pytest
+
+from comm_fusion_amd import build
+
+_VREG = re.compile(r"^v\[(\d+):(\d+)\]$|^v(\d+)$")
+_LGKM = re.compile(r"lgkmcnt\((\d+)\)")
+
+
+def _vregs(tok: str):
+    m = _VREG.match(tok)
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
+def _operands(line: str):
+    parts = line.split(None, 1)
+    if len(parts) < 2:
+        return parts[0], []
+    return parts[0], [o.strip().split()[0] for o in parts[1].split(",") if o.strip()]
+
+
+def _kernel_bodies(asm: str):
+    """{kernel symbol: [instruction and label lines]} for the attention kernels."""
+    out = {}
+    name = None
+    for raw in asm.splitlines():
+        line = raw.split(";")[0].strip()
+        m = re.match(r"^(_Z\S*attn_fwd\S*):$", line)
+        if m:
+            name = m.group(1)
+            out[name] = []
+            continue
+        if name is None:
+            continue
+        if line.startswith(".Lfunc_end"):  # blocks may follow an s_endpgm
+            name = None
+            continue
+        if line and not line.startswith("."):
+            out[name].append(line)
+        elif re.match(r"^\.LBB\w+:$", line):
+            out[name].append(line)
+    return out
+
+
+def _blocks(lines):
+    """Basic blocks: (instructions with their line index, successor block ids)."""
+    blocks, labels = [], {}
+    cur = []
+    for i, line in enumerate(lines):
+        if line.endswith(":"):
+            if cur:
+                blocks.append(cur)
+                cur = []
+            labels[line[:-1]] = len(blocks)
+            continue
+        cur.append((i, line))
+        if line.startswith(("s_branch", "s_cbranch", "s_endpgm", "s_setpc")):
+            blocks.append(cur)
+            cur = []
+    if cur:
+        blocks.append(cur)
+    # labels that precede an empty run map to the next block
+    succ = []
+    for k, blk in enumerate(blocks):
+        last = blk[-1][1] if blk else ""
+        op, ops = _operands(last) if blk else ("", [])
+        s = []
+        if op.startswith(("s_branch", "s_cbranch")):
+            s.append(labels[ops[0]])
+        if not op.startswith(("s_branch", "s_endpgm", "s_setpc")) and k + 1 < len(blocks):
+            s.append(k + 1)
+        succ.append(s)
+    return blocks, succ
+
+
+_MAXPEND = 32
+
+
+def _merge(a, b):
+    """Pending reads after either of two paths: entries aligned from the newest."""
+    if a is None:
+        return b
+    n = max(len(a), len(b))
+    pa = [frozenset()] * (n - len(a)) + list(a)
+    pb = [frozenset()] * (n - len(b)) + list(b)
+    return tuple(x | y for x, y in zip(pa, pb))
+
+
+def _step(state, line, bad, i):
+    op, ops = _operands(line)
+    if op.startswith("s_waitcnt"):
+        m = _LGKM.search(line)
+        if m:
+            n = int(m.group(1))
+            state = state[len(state) - n:] if n else ()
+        return state
+    touched = set()
+    for o in ops:
+        touched |= _vregs(o)
+    busy = set().union(*state) if state else set()
+    if touched & busy and bad is not None:
+        bad.append((i, line))
+    if op.startswith(("ds_read", "ds_load")):
+        state = state + (frozenset(_vregs(ops[0])),)
+    elif op.startswith(("ds_", "s_load", "s_buffer_load")):
+        state = state + (frozenset(),)
+    return state[-_MAXPEND:]
+
+
+def early_uses(lines):
+    """Instructions that read or write a VGPR of an LDS read not yet waited for.
+
+    LDS reads complete in issue order, so ``lgkmcnt(N)`` leaves the newest N
+    outstanding.  Scalar loads share the counter; they are counted in order
+    too, which only makes the check stricter.  The reads still in flight are
+    propagated over the control-flow graph (branches, fall-through, loop
+    back edges) to a fixed point; where paths join, either path's reads
+    count as in flight.
+    """
+    blocks, succ = _blocks(lines)
+    inn = [None] * len(blocks)
+    inn[0] = ()
+    work = [0]
+    while work:
+        k = work.pop()
+        st = inn[k]
+        for i, line in blocks[k]:
+            st = _step(st, line, None, i)
+        for t in succ[k]:
+            m = _merge(inn[t], st)
+            if m != inn[t]:
+                inn[t] = m
+                work.append(t)
+    bad = []
+    for k, blk in enumerate(blocks):
+        st = inn[k] if inn[k] is not None else ()
+        for i, line in blk:
+            st = _step(st, line, bad, i)
+    return bad
+
+
+@pytest.fixture(scope="module")
+def asm():
+    return build.assembly()
+
+
+def test_kernels_do_not_spill(asm):
+    meta = re.findall(r"\.name:\s+(_Z\S*attn_fwd\S*)|\.(vgpr_spill_count|private_segment_fixed_size):\s+(\d+)",
+                      asm)
+    assert any(name for name, _, _ in meta), "no attention kernels in the assembly"
+    spills = [(k, v) for _, k, v in meta if k and int(v) != 0]
+    assert not spills, spills
+
+
+def test_no_use_of_lds_results_before_their_wait(asm):
+    bodies = _kernel_bodies(asm)
+    assert len(bodies) >= 4, sorted(bodies)
+    for name, lines in bodies.items():
+        assert sum(l.startswith("ds_read") for l in lines) > 0, name
+        bad = early_uses(lines)
+        assert not bad, "%s: %s" % (name, bad[:5])
+
+
+def test_early_use_checker_catches_a_spill_before_the_wait():
+    # the pattern the check exists for: an asm LDS read's destination stored
+    # to scratch before its lgkmcnt wait
+    lines = ["ds_read_b128 v[96:99], v32 offset:0",
+             "scratch_store_dwordx4 off, v[96:99], off offset:140",
+             "s_waitcnt lgkmcnt(0)"]
+    assert early_uses(lines) == [(1, lines[1])]
+    ok = ["ds_read_b128 v[96:99], v32 offset:0",
+          "ds_read_b128 v[100:103], v32 offset:1024",
+          "s_waitcnt lgkmcnt(1)",
+          "v_mfma_f32_32x32x16_bf16 v[0:15], v[96:99], v[200:203], v[0:15]",
+          "s_waitcnt lgkmcnt(0)",
+          "v_mov_b32_e32 v5, v101"]
+    assert early_uses(ok) == []
+    # a wait that leaves the read outstanding does not cover it
+    late = ["ds_read_b128 v[96:99], v32", "s_waitcnt lgkmcnt(1)", "v_mov_b32_e32 v5, v97"]
+    assert early_uses(late) == [(2, late[2])]
