@@ -15,7 +15,9 @@ starts.  Prints ONE JSON line:
             interleaved rounds), the residual (fused - alone) / alone, the
             permute's and the epilogue layout's HBM rates, and from one traced
             fused call the per-work-unit epilogue store spans and the shader
-            clock the kernel ran at;
+            clock the kernel ran at; with both exchanges (detail.io): the
+            call that reads Q, K, V in place from the sequence-partitioned
+            inputs vs three separate gathers + attention + permute;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-io", action="store_true",
+                    help="skip the timings with the pre-attention exchange (detail.io)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--rounds", type=int, default=5,
@@ -269,6 +273,27 @@ def main():
         alone()
         perm()
 
+    fns = {"fused": fused, "serial": serial, "alone": alone, "perm": perm, "store_only": store_only}
+    if not args.no_io:
+        # Sequence-partitioned inputs [B][P][S/P][H][d] holding the rank's
+        # Q, K, V in its head slots (the other heads are never read).
+        lo, hi = w.rank * w.Hl, (w.rank + 1) * w.Hl
+        xs = []
+        for t in (q, k, v):
+            X = torch.zeros((w.B, w.S, w.H, w.d), dtype=torch.bfloat16, device=dev)
+            X[:, :, lo:hi] = t.view(w.B, w.S, w.Hl, w.d)
+            xs.append(X)
+        g_loc = [torch.empty_like(q) for _ in range(3)]
+        fns["fused_io"] = lambda: ua.attn_ulysses_fused_io(xs[0], xs[1], xs[2], w.rank, w.P, dest)
+        fns["gather"] = lambda: ua.a2a_gather(xs[0], w.rank, w.P, g_loc[0])
+
+        def serial_io():
+            for X, L in zip(xs, g_loc):
+                ua.a2a_gather(X, w.rank, w.P, L)
+            ua.attn_serial(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local)
+            perm()
+        fns["serial_io"] = serial_io
+
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
         src.fill_(1)
@@ -282,8 +307,7 @@ def main():
     # Baselines: fused, serial (attention + separate permute), attention
     # alone and permute alone, in interleaved rounds.
     reps = max(2, min(args.steps, int(200.0 / max(float(np.mean(per)), 1e-3)) + 1))
-    cmp = interleaved({"fused": fused, "serial": serial, "alone": alone, "perm": perm,
-                       "store_only": store_only}, args.rounds, reps)
+    cmp = interleaved(fns, args.rounds, reps)
     per_serial, per_alone, per_perm = cmp["serial"], cmp["alone"], cmp["perm"]
     tr = traced_call(ua, torch, q, k, v, w, scratch_dest)
 
@@ -294,6 +318,16 @@ def main():
     med = lambda x: float(np.median(x))  # noqa: E731
     t_f, t_s, t_a, t_p = med(cmp["fused"]), med(per_serial), med(per_alone), med(per_perm)
     traffic = measured_traffic(launch_ms)
+    io = None
+    if not args.no_io:
+        t_fio, t_sio, t_g = med(cmp["fused_io"]), med(cmp["serial_io"]), med(cmp["gather"])
+        io = {"fused_io_ms_median": round(t_fio, 4),
+              "serial_io_ms_median": round(t_sio, 4),
+              "gather_ms_median": round(t_g, 4),
+              "gather_hbm_GBs": round(2 * w.out_bytes / (t_g * 1e-3) / 1e9, 1),
+              "speedup_serial_io_over_fused_io": round(t_sio / t_fio, 4),
+              "residual_fused_io_vs_alone": round((t_fio - t_a) / t_a, 4),
+              "fused_io_TFLOPs": round(w.flops / (t_fio * 1e-3) / 1e12, 2)}
 
     out = {
         "metric": METRIC,
@@ -331,6 +365,7 @@ def main():
             # the same against the peak scaled to the clock the traced call ran at
             "pct_bf16_peak_at_traced_clock": round(100.0 * value / (PEAK_BF16_TFLOPS * tr["sclk_mhz_trace"] / 2400.0), 2)
             if tr.get("sclk_mhz_trace") else None,
+            "io": io,
             "wall_ms_timed_region": round(wall_ms, 3),
             "kernel_source_sha256_16": source_digest(),
         },

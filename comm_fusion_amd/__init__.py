@@ -11,16 +11,20 @@ Names and arguments follow the C calls:
   attn_ulysses_fused(Q, K, V, rank, P, out, scale=None, stream=None)
   attn_serial(Q, K, V, rank, P, O_local, scale=None, stream=None)
   a2a_permute(O_local, rank, P, out, stream=None)
+  attn_ulysses_fused_io(Xq, Xk, Xv, rank, P, out, scale=None, stream=None)
+  a2a_gather(X, rank, P, X_local, stream=None)
 and, for measurement only,
   attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None)
   epilogue_store_only(B, S, H, d, rank, P, out, stream=None)
   work_units(B, S, H, d, P)
 Tensors are torch tensors on the GPU: Q, K, V, O_local bfloat16
 [B][S][Hl][d]; out bfloat16 with B*S*(Hl*P)*d elements, laid out
-[B][P][S/P][H][d].
+[B][P][S/P][H][d]; Xq, Xk, Xv, X bfloat16 in the sequence-partitioned layout
+[B][P][S/P][H][d] (or the same bytes viewed as [B][S][H][d]).
 """
 from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # noqa: F401
-                       UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_OK, UAError, a2a_permute,
-                       attn_serial, attn_ulysses_fused, attn_ulysses_fused_trace, dest_bytes,
+                       UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_OK, UAError, a2a_gather, a2a_permute,
+                       attn_serial, attn_ulysses_fused, attn_ulysses_fused_io,
+                       attn_ulysses_fused_trace, dest_bytes,
                        epilogue_store_only, lib, lib_path, local_bytes, status_string, version,
                        work_units)

@@ -66,6 +66,10 @@ def lib() -> ctypes.CDLL:
     L.ua_epilogue_store_only.restype = i
     L.ua_work_units.argtypes = [sp, i]
     L.ua_work_units.restype = ctypes.c_int64
+    L.attn_ulysses_fused_io.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
+    L.attn_ulysses_fused_io.restype = i
+    L.a2a_gather.argtypes = [vp, i, i, vp, sp, vp]
+    L.a2a_gather.restype = i
     _lib = L
     return L
 
@@ -152,6 +156,46 @@ def a2a_permute(O_local, rank, P, out, stream=None):
                            _stream(stream))
     if st != UA_OK:
         raise UAError("a2a_permute", st)
+
+
+def _seq_shape(X, P):
+    """Shape of a sequence-partitioned input, [B][P][S/P][H][d] or (the same
+    bytes) [B][S][H][d]."""
+    if X.dim() == 5:
+        B, P_, Sp, H, d = (int(x) for x in X.shape)
+        if P_ != int(P):
+            raise ValueError("X has %d regions, expected P = %d" % (P_, int(P)))
+        return Shape(B, P_ * Sp, H, d)
+    if X.dim() == 4:
+        B, S, H, d = (int(x) for x in X.shape)
+        return Shape(B, S, H, d)
+    raise ValueError("X must be [B][P][S/P][H][d] or [B][S][H][d]")
+
+
+def attn_ulysses_fused_io(Xq, Xk, Xv, rank, P, out, scale=None, stream=None):
+    """Both exchanges fused: this rank's heads read in place from the
+    sequence-partitioned ``Xq, Xk, Xv``, output into ``out`` [B][P][S/P][H][d]."""
+    shp = _seq_shape(Xq, P)
+    n = shp.B * shp.S * shp.H * shp.d
+    for nm, t in (("Xq", Xq), ("Xk", Xk), ("Xv", Xv)):
+        _check_bf16(nm, t, n)
+    _check_bf16("out", out, n)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_ulysses_fused_io(_ptr(Xq), _ptr(Xk), _ptr(Xv), int(rank), int(P), _ptr(out),
+                                     ctypes.byref(shp), scale, _stream(stream))
+    if st != UA_OK:
+        raise UAError("attn_ulysses_fused_io", st)
+
+
+def a2a_gather(X, rank, P, X_local, stream=None):
+    """Serial pre-attention All-to-All: this rank's heads of ``X`` into
+    ``X_local`` [B][S][Hl][d]."""
+    shp = _seq_shape(X, P)
+    _check_bf16("X", X, shp.B * shp.S * shp.H * shp.d)
+    _check_bf16("X_local", X_local, shp.B * shp.S * (shp.H // int(P)) * shp.d)
+    st = lib().a2a_gather(_ptr(X), int(rank), int(P), _ptr(X_local), ctypes.byref(shp), _stream(stream))
+    if st != UA_OK:
+        raise UAError("a2a_gather", st)
 
 
 def work_units(B, S, H, d, P) -> int:

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
@@ -56,6 +56,14 @@ int check_limits(const ua_shape *shp, int P)
     return UA_OK;
 }
 
+// The sequence-partitioned input [B][P][S/P][H][d] is read in place with a
+// row stride of H*d elements: a 64-row K/V tile must span fewer than 2^31 bytes.
+int check_limits_seq(const ua_shape *shp)
+{
+    if (shp->H * shp->d > (int64_t)1 << 24) return UA_ERR_UNSUPPORTED;
+    return UA_OK;
+}
+
 bool empty(const ua_shape *shp) { return shp->B == 0 || shp->S == 0; }
 
 ua::Placement dest_placement(void *out, const ua_shape *shp, int rank, int P)
@@ -80,23 +88,29 @@ ua::Placement local_placement(void *o_local, const ua_shape *shp, int P)
     return o;
 }
 
+// seq_input: Q, K, V are the sequence-partitioned [B][P][S/P][H][d] inputs
+// of the pre-attention exchange (read in place), else [B][S][Hl][d].
 int attention_call(const void *Q, const void *K, const void *V, int rank, int P, void *out,
                    const ua_shape *shp, float scale, void *stream, bool fused, uint64_t *trace = nullptr,
-                   bool want_trace = false)
+                   bool want_trace = false, bool seq_input = false)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);
     if (st != UA_OK) return st;
     if (!isfinite(scale) || !(scale > 0.0f)) return UA_ERR_UNSUPPORTED;
     if ((st = check_limits(shp, P)) != UA_OK) return st;
+    if (seq_input && (st = check_limits_seq(shp)) != UA_OK) return st;
     if (empty(shp)) return UA_OK;
     if (!Q || !K || !V || !out || (want_trace && !trace)) return UA_ERR_NULL;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || (want_trace && !aligned16(trace)))
         return UA_ERR_ALIGN;
     const ua::Placement o = fused ? dest_placement(out, shp, rank, P) : local_placement(out, shp, P);
+    const int64_t Hl = shp->H / P;
+    const int64_t in_heads = seq_input ? shp->H : Hl;
+    const int64_t in_head0 = seq_input ? (int64_t)rank * Hl : 0;
     const hipError_t e = ua::launch_attention((const uint16_t *)Q, (const uint16_t *)K,
-                                              (const uint16_t *)V, shp->B, shp->S, shp->H / P,
-                                              (int)shp->d, scale, o, (hipStream_t)stream, trace);
+                                              (const uint16_t *)V, in_heads, in_head0, shp->B, shp->S,
+                                              Hl, (int)shp->d, scale, o, (hipStream_t)stream, trace);
     return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
@@ -114,6 +128,28 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P, vo
                 const ua_shape *shp, float scale, void *stream)
 {
     return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false);
+}
+
+int attn_ulysses_fused_io(const void *Xq, const void *Xk, const void *Xv, int rank, int P, void *out,
+                          const ua_shape *shp, float scale, void *stream)
+{
+    return attention_call(Xq, Xk, Xv, rank, P, out, shp, scale, stream, true, nullptr, false, true);
+}
+
+int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *shp, void *stream)
+{
+    int64_t elems = 0;
+    int st = check_shape(shp, rank, P, &elems);
+    if (st != UA_OK) return st;
+    if ((st = check_limits(shp, P)) != UA_OK) return st;
+    if (empty(shp)) return UA_OK;
+    if (!X || !X_local) return UA_ERR_NULL;
+    if (!aligned16(X) || !aligned16(X_local)) return UA_ERR_ALIGN;
+    // the source is described like the exchange's destination; only read
+    const ua::Placement in = dest_placement(const_cast<void *>(X), shp, rank, P);
+    const hipError_t e = ua::launch_gather(in, shp->B, shp->S, shp->H / P, (int)shp->d,
+                                           (uint16_t *)X_local, (hipStream_t)stream);
+    return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
 int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int rank, int P, void *out,

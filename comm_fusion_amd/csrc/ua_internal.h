@@ -23,11 +23,15 @@ struct Placement {
     int64_t head0;
 };
 
-// Attention over Hl local heads of [B][S][Hl][d] Q, K, V (bf16 bits).  With
-// a non-null trace, the measurement build runs and fills 4 uint64 per unit.
+// Attention over Hl local heads (bf16 bits).  Q, K, V are [B][S][in_heads][d]
+// with this rank's heads at in_head0 .. in_head0+Hl-1: in_heads = Hl,
+// in_head0 = 0 for the local layout [B][S][Hl][d]; in_heads = H,
+// in_head0 = rank*Hl for the sequence-partitioned input [B][P][S/P][H][d].
+// With a non-null trace, the measurement build runs and fills 4 uint64 per unit.
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                            int64_t B, int64_t S, int64_t Hl, int d, float scale,
-                            const Placement &out, hipStream_t stream, uint64_t *trace = nullptr);
+                            int64_t in_heads, int64_t in_head0, int64_t B, int64_t S, int64_t Hl,
+                            int d, float scale, const Placement &out, hipStream_t stream,
+                            uint64_t *trace = nullptr);
 
 // The attention kernel's epilogue stores alone (closed-form values).
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
@@ -36,6 +40,11 @@ hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const P
 // Bit copy of O_local [B][S][Hl][d] rows into `out`.
 hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t Hl, int d,
                           const Placement &out, hipStream_t stream);
+
+// Bit copy of this rank's rows of a sequence-partitioned input (placed as
+// `in` describes; base is only read) into x_local [B][S][Hl][d].
+hipError_t launch_gather(const Placement &in, int64_t B, int64_t S, int64_t Hl, int d,
+                         uint16_t *x_local, hipStream_t stream);
 
 // Work units (one workgroup each) the attention launch uses for this shape.
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);

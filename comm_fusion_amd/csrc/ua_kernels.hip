@@ -72,6 +72,8 @@ struct AttnArgs {
     Placement out;
     int64_t S;
     int32_t Hl;
+    int32_t in_heads;  // heads per sequence row of Q, K, V (Hl, or H for the pre-exchange layout)
+    int32_t in_head0;  // this rank's first head among them (0, or rank*Hl)
     int32_t n_qtiles;
     int32_t n_units;
     float scale_log2;  // softmax scale * log2(e)
@@ -204,8 +206,12 @@ void attn_fwd(AttnArgs a)
     const int h = bh % a.Hl;
     const int64_t b = bh / a.Hl;
     const int64_t S = a.S;
-    const int rs = a.Hl * D;  // elements between sequence rows
-    const int64_t head = (b * S * a.Hl + h) * D;
+    // Q, K, V rows: [B][S][in_heads][D], this unit's head at in_head0 + h.
+    // With in_heads = H this is the sequence-partitioned input of the
+    // pre-attention exchange, [B][P][S/P][H][D] (source rank p's rows
+    // [p*S/P, (p+1)*S/P) back to back), read in place.
+    const int rs = a.in_heads * D;  // elements between sequence rows
+    const int64_t head = (b * S * a.in_heads + a.in_head0 + h) * D;
     const uint16_t *qh = a.q + head;
     const uint16_t *kh = a.k + head;
     const uint16_t *vh = a.v + head;
@@ -697,6 +703,27 @@ __global__ __launch_bounds__(256) void permute_rows(const uint16_t *src, uint32_
     *(u32x4 *)dst = *(const u32x4 *)(src + (int64_t)c * 8);
 }
 
+// Serial pre-attention All-to-All: each thread copies one 16-byte chunk of
+// X_local [B][S][Hl][d] from its slot of the sequence-partitioned input
+// (described by a Placement like the exchange's destination: row s of local
+// head h sits in region p = s / region_rows, row i, head head0 + h).  For a
+// fixed (b, s) the Hl*d elements are contiguous on both sides.
+__global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chunks,
+                                                   uint32_t chunks_per_slab, uint32_t S,
+                                                   uint16_t *dst, int d)
+{
+    const uint32_t c = blockIdx.x * 256u + threadIdx.x;
+    if (c >= n_chunks) return;
+    const uint32_t slab = c / chunks_per_slab;       // = b*S + s
+    const uint32_t within = c - slab * chunks_per_slab;
+    const uint32_t b = slab / S, s = slab - b * S;
+    const uint32_t p = s / (uint32_t)in.region_rows;
+    const uint32_t i = s - p * (uint32_t)in.region_rows;
+    const uint16_t *src = in.base + ((((int64_t)b * in.regions + p) * in.region_rows + i) * in.heads +
+                                     in.head0) * d + (int64_t)within * 8;
+    *(u32x4 *)(dst + (int64_t)c * 8) = *(const u32x4 *)src;
+}
+
 // Waves per workgroup for a shape: 8 (one K/V tile per 256 query rows) when
 // that still gives at least half a workgroup per CU, else 4.
 int waves_for(int64_t B, int64_t S, int64_t Hl, int d)
@@ -715,8 +742,9 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                            int64_t B, int64_t S, int64_t Hl, int d, float scale,
-                            const Placement &out, hipStream_t stream, uint64_t *trace)
+                            int64_t in_heads, int64_t in_head0, int64_t B, int64_t S, int64_t Hl,
+                            int d, float scale, const Placement &out, hipStream_t stream,
+                            uint64_t *trace)
 {
     const int nw = waves_for(B, S, Hl, d);
     AttnArgs a;
@@ -726,6 +754,8 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.out = out;
     a.S = S;
     a.Hl = (int32_t)Hl;
+    a.in_heads = (int32_t)in_heads;
+    a.in_head0 = (int32_t)in_head0;
     a.n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
     a.n_units = (int32_t)attention_units(B, S, Hl, d);
     a.scale_log2 = scale * 1.4426950408889634f;
@@ -767,6 +797,20 @@ hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t
     const uint16_t *src = o_local;
     void *args[] = {(void *)&src, &n, &cps, &S32, &o, &d32};
     return hipLaunchKernel((const void *)permute_rows, dim3((n + 255) / 256), dim3(256), args, 0,
+                           stream);
+}
+
+hipError_t launch_gather(const Placement &in, int64_t B, int64_t S, int64_t Hl, int d,
+                         uint16_t *x_local, hipStream_t stream)
+{
+    uint32_t cps = (uint32_t)(Hl * d / 8);
+    uint32_t n = (uint32_t)(B * S * cps);
+    uint32_t S32 = (uint32_t)S;
+    int d32 = d;
+    Placement i = in;
+    uint16_t *dst = x_local;
+    void *args[] = {&i, &n, &cps, &S32, (void *)&dst, &d32};
+    return hipLaunchKernel((const void *)gather_rows, dim3((n + 255) / 256), dim3(256), args, 0,
                            stream);
 }
 

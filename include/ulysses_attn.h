@@ -18,6 +18,10 @@
  *
  * Layouts (bf16 = IEEE binary16-brain, passed as raw 16-bit patterns):
  *   Q, K, V, O_local : [B][S][Hl][d], contiguous, Hl = H / P.
+ *   Xq, Xk, Xv, X (sequence-partitioned, before the pre-attention exchange):
+ *       [B][P][S/P][H][d], contiguous: region p is source rank p's chunk of
+ *       sequence rows [p*S/P, (p+1)*S/P) with all H heads; this rank's heads
+ *       are g = rank*Hl .. rank*Hl+Hl-1.
  *   out (destination): [B][P][S/P][H][d], contiguous: P back-to-back regions,
  *       region p holding sequence rows [p*S/P, (p+1)*S/P) of all H heads.
  *       Row s of local head h_l lands in region p = s / (S/P), local row
@@ -42,7 +46,8 @@
  * otherwise NULL buffers (UA_ERR_NULL) and alignment (UA_ERR_ALIGN).  A
  * launch failure reported by the runtime gives UA_ERR_HIP.  Size limits
  * (UA_ERR_UNSUPPORTED beyond them): B*S*Hl < 2^31 rows, B*S*Hl*d/8 < 2^32
- * 16-byte chunks, Hl*d <= 2^24 elements per sequence row.
+ * 16-byte chunks, Hl*d <= 2^24 elements per sequence row (H*d <= 2^24 for
+ * attn_ulysses_fused_io, which reads the sequence-partitioned rows in place).
  */
 #ifndef ULYSSES_ATTN_H
 #define ULYSSES_ATTN_H
@@ -99,6 +104,25 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P,
 int a2a_permute(const void *O_local, int rank, int P, void *out,
                 const ua_shape *shp, void *stream);
 
+/*
+ * Both exchanges fused.  Fig. 5 steps (a)-(c) of the review page: the
+ * pre-attention All-to-All turns the sequence-partitioned projections into
+ * head partitions; here, instead of a separate gather, the attention
+ * kernel's Q load and K/V tile copies read this rank's heads straight from
+ * the P source regions of Xq, Xk, Xv ([B][P][S/P][H][d]; the other heads'
+ * bytes are never read).  The output side is attn_ulysses_fused's.  The
+ * result is bit-identical to a2a_gather of Xq, Xk and Xv followed by
+ * attn_ulysses_fused.  Validation as attn_ulysses_fused, plus H*d <= 2^24.
+ */
+int attn_ulysses_fused_io(const void *Xq, const void *Xk, const void *Xv, int rank, int P,
+                          void *out, const ua_shape *shp, float scale, void *stream);
+/*
+ * Serial baseline of the pre-attention exchange (Fig. 5 steps a-c, run as a
+ * separate step): copies this rank's Hl heads of every row of X
+ * [B][P][S/P][H][d] bit-for-bit into X_local [B][S][Hl][d] (row s from
+ * region s / (S/P), local row s mod (S/P)).  Validation as a2a_permute.
+ */
+int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *shp, void *stream);
 /*
  * Measurement build of attn_ulysses_fused (the per-tile store spans the
  * pages time for the piggybacked epilogue; review page, Fig. 7): the same

@@ -183,6 +183,29 @@ void oracle_dest_offsets(const int64_t *rows, int64_t nrows,
 }
 
 /*
+ * The pre-attention All-to-All for one rank (Fig. 5, steps a-c: sequence
+ * partitions become head partitions) as a plain copy.  Before it, source rank
+ * p holds rows [p*S/P, (p+1)*S/P) of all H heads; laid out as P adjacent
+ * regions this is the same [B][P][S/P][H][d] buffer as the destination of the
+ * post-attention exchange, so row (b, s, h_l) of this rank's X_local
+ * [B][S][Hl][d] is read from oracle_dest_offset(b, s, h_l, ...).  Returns 0 or -1.
+ */
+int oracle_gather(const uint16_t *X, int64_t B, int64_t S, int64_t H, int64_t d,
+                  int64_t P, int64_t rank, uint16_t *X_local)
+{
+    if (P <= 0 || H % P != 0 || S % P != 0 || rank < 0 || rank >= P) return -1;
+    int64_t Hl = H / P;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t s = 0; s < S; ++s)
+            for (int64_t h = 0; h < Hl; ++h) {
+                int64_t off = oracle_dest_offset(b, s, h, B, S, H, d, P, rank);
+                memcpy(X_local + bshd(b, s, h, 0, S, Hl, d), X + off,
+                       (size_t)d * sizeof(uint16_t));
+            }
+    return 0;
+}
+
+/*
  * The serial All-to-All as a plain copy: every row (b, s, h_l) of the local
  * output O_local [B][S][Hl][d] is copied bit-for-bit to its destination slot.
  * Slots of other ranks' heads are not touched.  Returns 0 or -1.

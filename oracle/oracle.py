@@ -9,7 +9,9 @@ plain softmax-attention definition that FlashAttention computes exactly (up to
 rounding), and the placement is the post-attention All-to-All of Fig. 5 on the
 pith.science review page (steps d-e), read as: rank r owns heads
 [r*H/P, (r+1)*H/P), destination rank p owns rows [p*S/P, (p+1)*S/P), and the
-destination buffer is laid out [B][P][S/P][H][d].
+destination buffer is laid out [B][P][S/P][H][d].  The pre-attention exchange
+(steps a-c) is read the same way in reverse: source rank p holds rows
+[p*S/P, (p+1)*S/P) of all heads, the P chunks laid out [B][P][S/P][H][d].
 """
 from __future__ import annotations
 
@@ -63,6 +65,8 @@ def _load():
     lib.oracle_dest_offsets.restype = None
     lib.oracle_permute.argtypes = [u16p, i64, i64, i64, i64, i64, i64, u16p]
     lib.oracle_permute.restype = ctypes.c_int
+    lib.oracle_gather.argtypes = [u16p, i64, i64, i64, i64, i64, i64, u16p]
+    lib.oracle_gather.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -142,6 +146,26 @@ def dest_offsets(rows, B, S, H, d, P, rank) -> np.ndarray:
     out = np.empty(rows.shape[0], dtype=np.int64)
     _load().oracle_dest_offsets(_ptr(rows, ctypes.c_int64), rows.shape[0],
                                 B, S, H, d, P, rank, _ptr(out, ctypes.c_int64))
+    return out
+
+
+def gather(X, H, P, rank) -> np.ndarray:
+    """This rank's heads of the sequence-partitioned X [B][P][S/P][H][d] (or the
+    same bytes as [B][S][H][d]) as X_local [B][S][Hl][d] (bit copy)."""
+    X = _u16(X)
+    if X.ndim == 5:
+        B, P_, Sp, H_, d = X.shape
+        S = P_ * Sp
+    else:
+        B, S, H_, d = X.shape
+        P_ = P
+    if H_ != H or P_ != P or H % P != 0:
+        raise ValueError("shape mismatch between X, H and P")
+    out = np.empty((B, S, H // P, d), dtype=np.uint16)
+    rc = _load().oracle_gather(_ptr(X, ctypes.c_uint16), B, S, H, d, P, rank,
+                               _ptr(out, ctypes.c_uint16))
+    if rc != 0:
+        raise ValueError("oracle_gather rejected its arguments")
     return out
 
 

@@ -42,7 +42,7 @@ def test_status_codes_match_header():
         assert getattr(ua, name) == val
         assert ua.status_string(val) and ua.status_string(val) != "unknown status"
     assert ua.status_string(12345) == "unknown status"
-    assert ua.version() == 10000
+    assert ua.version() == 10100
 
 
 def _fused(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
@@ -55,11 +55,20 @@ def _serial(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
     return L.attn_serial(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale, None)
 
 
+def _fused_io(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
+    L = ua.lib()
+    return L.attn_ulysses_fused_io(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale, None)
+
+
 def _permute(shape, rank=0, P=2, src=A, out=O):
     return ua.lib().a2a_permute(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
 
 
-@pytest.mark.parametrize("call", [_fused, _serial])
+def _gather(shape, rank=0, P=2, src=A, out=O):
+    return ua.lib().a2a_gather(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
+
+
+@pytest.mark.parametrize("call", [_fused, _serial, _fused_io])
 def test_attention_argument_validation(call):
     good = (1, 64, 4, 64)
     assert ua.lib().attn_ulysses_fused(A, B_, C, 0, 2, O, None, 0.1, None) == ua.UA_ERR_NULL
@@ -86,21 +95,34 @@ def test_attention_argument_validation(call):
     assert call((0, 1, 1 << 17, 128), P=1) == ua.UA_OK  # Hl*d = 2^24 is allowed
 
 
-@pytest.mark.parametrize("call", [_fused, _serial, _permute])
+@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _permute, _gather])
 def test_empty_calls_succeed_without_touching_memory(call):
-    assert call((0, 64, 4, 64), src=0, out=0) == ua.UA_OK if call is _permute else \
+    copy = call in (_permute, _gather)
+    assert call((0, 64, 4, 64), src=0, out=0) == ua.UA_OK if copy else \
         call((0, 64, 4, 64), q=0, k=0, v=0, out=0) == ua.UA_OK
-    assert call((3, 0, 4, 128), src=0, out=0) == ua.UA_OK if call is _permute else \
+    assert call((3, 0, 4, 128), src=0, out=0) == ua.UA_OK if copy else \
         call((3, 0, 4, 128), q=0, k=0, v=0, out=0) == ua.UA_OK
 
 
-def test_permute_argument_validation():
+@pytest.mark.parametrize("call", [_permute, _gather])
+def test_exchange_copy_argument_validation(call):
     good = (2, 64, 8, 128)
-    assert _permute(good, src=0) == ua.UA_ERR_NULL
-    assert _permute((2, 60, 8, 128), P=8) == ua.UA_ERR_SHAPE
-    assert _permute(good, rank=5, P=4) == ua.UA_ERR_RANK
-    assert _permute(good, src=A + 4) == ua.UA_ERR_ALIGN
-    assert _permute((2, 64, 8, 32)) == ua.UA_ERR_UNSUPPORTED
+    assert call(good, src=0) == ua.UA_ERR_NULL
+    assert call(good, out=0) == ua.UA_ERR_NULL
+    assert call((2, 60, 8, 128), P=8) == ua.UA_ERR_SHAPE
+    assert call(good, rank=5, P=4) == ua.UA_ERR_RANK
+    assert call(good, src=A + 4) == ua.UA_ERR_ALIGN
+    assert call(good, out=O + 8) == ua.UA_ERR_ALIGN
+    assert call((2, 64, 8, 32)) == ua.UA_ERR_UNSUPPORTED
+
+
+def test_fused_io_limits_the_full_row_stride():
+    # Hl*d = 2^24 passes every call; H*d = 2^25 is beyond the in-place read of
+    # the sequence-partitioned input, so only attn_ulysses_fused_io rejects it
+    shape = (0, 2, 1 << 18, 128)
+    assert _fused(shape, q=0, k=0, v=0, out=0) == ua.UA_OK
+    assert _fused_io(shape, q=0, k=0, v=0, out=0) == ua.UA_ERR_UNSUPPORTED
+    assert _fused_io((0, 2, 1 << 17, 128), q=0, k=0, v=0, out=0) == ua.UA_OK
 
 
 def test_buffer_size_helpers():

@@ -96,3 +96,51 @@ def test_permute_copies_bits_and_leaves_other_slots():
     np.testing.assert_array_equal(view[:, :, r * Hl:(r + 1) * Hl], O)
     others = np.delete(view, np.s_[r * Hl:(r + 1) * Hl], axis=2)
     assert np.all(others == 0x7FD5)
+
+
+# ---- the pre-attention exchange (Fig. 5 steps a-c): source rank p holds rows
+# [p*S/P, (p+1)*S/P) of all H heads, laid out [B][P][S/P][H][d]; rank r takes
+# its heads [r*Hl, (r+1)*Hl) of every row.
+
+def test_gather_hand_worked_small_case():
+    # B=1, S=4, H=4, P=2, d=1, X[j] = j: X is [1][2][2][4][1], element
+    # (p, i, g) at (p*2 + i)*4 + g.  Rank 1 owns heads 2, 3; its row s comes
+    # from region p = s // 2, local row i = s % 2.  Worked by hand.
+    X = np.arange(16, dtype=np.uint16).reshape(1, 2, 2, 4, 1)
+    want = {0: [[0, 1], [4, 5], [8, 9], [12, 13]],
+            1: [[2, 3], [6, 7], [10, 11], [14, 15]]}
+    for r in (0, 1):
+        got = oracle.gather(X, 4, 2, r)
+        assert got.shape == (1, 4, 2, 1)
+        np.testing.assert_array_equal(got[0, :, :, 0], np.array(want[r], dtype=np.uint16))
+
+
+def test_gather_over_all_ranks_reassembles_the_input():
+    # concatenating every rank's heads restores X read as [B][S][H][d]
+    B, S, H, d, P = 2, 24, 6, 4, 3
+    X, _, _ = make_qkv(B, S, H, d, 41)
+    parts = [oracle.gather(X.reshape(B, P, S // P, H, d), H, P, r) for r in range(P)]
+    np.testing.assert_array_equal(np.concatenate(parts, axis=2), X)
+
+
+def test_gather_is_the_inverse_of_permute():
+    # gather then permute writes back exactly the rank's slots of X
+    B, S, H, d, P, r = 2, 16, 8, 8, 4, 3
+    X, _, _ = make_qkv(B, S, H, d, 42)
+    loc = oracle.gather(X, H, P, r)
+    dest = np.full(B * S * H * d, 0x7FD5, np.uint16)
+    oracle.permute(loc, H, P, r, dest)
+    view = dest.reshape(B, S, H, d)
+    Hl = H // P
+    np.testing.assert_array_equal(view[:, :, r * Hl:(r + 1) * Hl], X[:, :, r * Hl:(r + 1) * Hl])
+    assert np.all(np.delete(view, np.s_[r * Hl:(r + 1) * Hl], axis=2) == 0x7FD5)
+
+
+def test_gather_rejects_bad_arguments():
+    X = np.zeros((1, 8, 4, 8), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.gather(X, 4, 3, 0)        # H % P
+    with pytest.raises(ValueError):
+        oracle.gather(X, 4, 2, 2)        # rank >= P
+    with pytest.raises(ValueError):
+        oracle.gather(X, 6, 2, 0)        # H does not match X
