@@ -23,7 +23,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# UA_ORACLE_LIB points the loader at another build of attn_oracle.c (the
+# mutation test compiles deliberately broken copies and runs the pins on them).
+LIB_PATH = os.environ.get("UA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 _lib = None
 
