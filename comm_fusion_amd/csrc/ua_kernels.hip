@@ -1,6 +1,7 @@
 // ua_kernels.hip -- gfx950 (MI355X) kernels for one Ulysses rank's attention
-// with the post-attention All-to-All fused into the output epilogue, and the
-// stand-alone permute used by the serial baseline.
+// with the post-attention All-to-All fused into the output epilogue (and, on
+// request, the pre-attention one fused into its loads), plus the stand-alone
+// permute and gather used by the serial baselines.
 //
 // Method (X-Stage paper, arXiv 2607.23264): Fig. 5 of the pith.science review
 // page (Ulysses attention; steps d-e are attention plus the post-attention
@@ -34,7 +35,18 @@
 //    destination slot computed from (rank, P) -- the fused All-to-All.  The
 //    local (serial) output is the same epilogue with one region;
 //  * workgroup ids are remapped so that consecutive work units of one head
-//    run on the same XCD and share its L2 while they stream the same K/V.
+//    run on the same XCD and share its L2 while they stream the same K/V;
+//  * Q, K, V rows are read with a row stride of in_heads*d: the local layout
+//    [B][S][Hl][d], or this rank's heads of the sequence-partitioned input
+//    [B][P][S/P][H][d] of the pre-attention All-to-All (Fig. 5, steps a-c),
+//    read in place.
+//
+// The LDS operand reads are inline assembly with explicit lgkmcnt waits, so
+// the compiler believes their results exist as soon as they issue.  Nothing
+// may copy, spill or overwrite such a register before its wait: the wait is
+// tied to the very ring slot the read wrote, the ring is drained by a tied
+// wait before the final iteration, and the kernels must not spill (checked
+// on the assembly by the CPU tests).
 
 #include "ua_internal.h"
 
