@@ -191,22 +191,29 @@ def test_wide_rows_many_heads():
 
 
 @pytest.mark.parametrize("H,d", [(64, 128), (4, 64)])  # P = 2: 8-wave and 4-wave launches
-@pytest.mark.parametrize("pattern", ["rising", "spikes"])
+@pytest.mark.parametrize("pattern", ["rising", "spikes", "offset", "tiny"])
 def test_running_max_rises_and_jumps(H, d, pattern):
     # Scores whose running max keeps rising along the keys (K rows scaled by
     # 0.25 .. 3.25), or jumps far past it in the middle of the sequence (three
     # keys scaled by 60: against the earlier max, exp of such a score
     # overflows fp32 for a few percent of the rows).  The online softmax has to
     # raise its max and rescale in the middle KV tiles, not only at the ends.
+    # Also: every key shifted by a common vector (scores of a row sit up to a
+    # few hundred away from zero, far outside exp's fp32 range), and keys
+    # scaled down to ~1e-3 (nearly uniform weights).
     from ua_inputs import to_bf16_bits
     B, S, P, rank = 1, 1030, 2, 1
     Q, K, V = _case(B, S, H, P, rank, d, 12)
     Kf = bits_to_f64(K)
     if pattern == "rising":
         Kf *= (0.25 + 3.0 * np.arange(S) / S)[None, :, None, None]
-    else:
+    elif pattern == "spikes":
         for j in (200, 611, 777):
             Kf[:, j] *= 60.0
+    elif pattern == "offset":
+        Kf += 24.0 * np.sign(bits_to_f64(Q).mean(axis=1, keepdims=True))
+    else:
+        Kf *= 1e-3
     K = to_bf16_bits(Kf.astype(np.float32))
     scale = 1.0 / math.sqrt(d)
     dest = _fused(Q, K, V, rank, P, H)
