@@ -143,15 +143,15 @@ def source_digest() -> str:
         return hashlib.sha256(code_text(f.read()).encode()).hexdigest()[:16]
 
 
-def measured_traffic(launch_ms):
+def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, only if it
-    was taken on the current kernel source; otherwise None."""
+    was taken on this workload and on the current kernel code; otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("code_sha256_16") != source_digest():
+    if t.get("code_sha256_16") != source_digest() or t.get("workload_name") != workload:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -346,7 +346,7 @@ def main():
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     med = lambda x: float(np.median(x))  # noqa: E731
     t_f, t_s, t_a, t_p = med(cmp["fused"]), med(per_serial), med(per_alone), med(per_perm)
-    traffic = measured_traffic(launch_ms)
+    traffic = measured_traffic(w.name)
     io = None
     if not args.no_io:
         t_fio, t_sio, t_g = med(cmp["fused_io"]), med(cmp["serial_io"]), med(cmp["gather"])

@@ -28,3 +28,9 @@ def test_digest_ignores_comment_edits_but_not_code_edits(tmp_path, monkeypatch):
     k.write_text("// v1\nint f() { return 3; }\n")
     assert bench.source_digest() != d0
 
+
+
+def test_traffic_figures_apply_only_to_their_workload():
+    # the committed counter summary covers one workload; any other reports null
+    assert bench.measured_traffic("tiny") is None
+    assert bench.measured_traffic("no_such_workload") is None
