@@ -72,10 +72,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-constexpr int kBn = 64;        // keys per KV tile
-constexpr int kNB = kBn / 32;  // 32-key blocks per KV tile
 constexpr int kPF = 2;         // operand prefetch distance, in MFMAs
-constexpr int kRowsPerWave = 32;
 
 struct AttnArgs {
     const uint16_t *q;
@@ -171,15 +168,19 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
-// NW = 8: two waves per SIMD, one workgroup per CU.  NW = 4 only runs for
-// shapes with fewer work units than CUs, so it is built for one wave per SIMD
-// (and gets that SIMD's whole register file).
+// Template parameters: D head dim; NW waves per workgroup; RB 32-row query
+// blocks per wave; KB keys per K/V tile.  NW = 8: two waves per SIMD, one
+// workgroup per CU.  NW = 4 only runs for shapes with fewer work units than
+// CUs, so it is built for one wave per SIMD (and gets that SIMD's whole
+// register file).  RB = 2 (d = 64 only, where the registers allow it): each
+// K or V fragment read from LDS feeds two MFMAs, one per row block, which
+// halves the LDS operand bytes per flop.
 // TRACE: measurement build with the same arithmetic and output, which also
 // records per work unit (in a.trace[4*unit ..]): the 100 MHz constant clock
 // at the start, when every wave has its normalised rows ready (a workgroup
 // barrier), when every wave's epilogue stores have completed (vmcnt(0) and a
 // barrier), and the shader-clock cycles from start to end.
-template <int D, int NW, bool TRACE>
+template <int D, int NW, int RB, int KB, bool TRACE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd(AttnArgs a)
 {
@@ -188,13 +189,21 @@ void attn_fwd(AttnArgs a)
         tr_t0 = __builtin_amdgcn_s_memrealtime();
         tr_c0 = __builtin_amdgcn_s_memtime();
     }
-    constexpr int TILE = kBn * D * 2;        // bytes of one K (or V) tile
-    constexpr int NLD = TILE / (NW * 1024);  // 1 KiB global->LDS copies per wave
+    constexpr int KNB = KB / 32;             // 32-key blocks per K/V tile
+    constexpr int TILE = KB * D * 2;         // bytes of one K (or V) tile
+    constexpr int NCP = TILE / 1024;         // 1 KiB global->LDS copies per tile
+    // With at least as many copies as waves, every wave copies NLD chunks of
+    // K and of V; with fewer, waves [0, NCP) copy K and [NCP, 2 NCP) copy V.
+    constexpr bool SPLIT = NCP < NW;
+    constexpr int NLD = SPLIT ? 1 : NCP / NW;
+    constexpr int CPG = KB / 16;             // 1 KiB copies per 32-column group
     constexpr int KK = D / 16;               // MFMA k-steps over d for S^T
     constexpr int DB = D / 32;               // 32-row blocks of O^T over d
-    constexpr int GB = kBn * 64;             // bytes of one 32-column group of a tile
-    constexpr int BR = kRowsPerWave * NW;    // query rows per work unit
-    static_assert(NLD >= 1 && TILE % (NW * 1024) == 0, "tile split");
+    constexpr int GB = KB * 64;              // bytes of one 32-column group of a tile
+    constexpr int RW = 32 * RB;              // query rows per wave
+    constexpr int BR = RW * NW;              // query rows per work unit
+    static_assert(SPLIT ? 2 * NCP <= NW : NCP % NW == 0, "tile split");
+    static_assert(KB % 32 == 0 && GB == CPG * 1024, "tile geometry");
 
     // Three K and three V tile buffers (a ring: tile j lives in buffer j % 3).
     // Every LDS read in this kernel is an explicit instruction (lds_b128,
@@ -207,7 +216,7 @@ void attn_fwd(AttnArgs a)
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int il = lane & 31;  // query row of this lane within the wave
+    const int il = lane & 31;  // query row of this lane within each row block
     const int g = lane >> 5;   // half-wave
     const int i16 = lane & 15;
     const int half = (lane >> 4) & 1;
@@ -238,14 +247,18 @@ void attn_fwd(AttnArgs a)
     //   V tile: [group of 32 columns][key row][64 B]; a transposing read
     //     (8 rows x 64 B of one group per wave) is 512 contiguous bytes.
     // Each copy fetches 16 row segments of 64 contiguous bytes: 1 KiB copy
-    // number c (wave-uniform) covers group c / 4, rows 16*(c % 4) .. +15, and
-    // lane L takes row 16*(c % 4) + L/4, 16 B chunk L % 4 of the segment.  The
+    // number c covers group c / CPG, rows 16*(c % CPG) .. +15, and lane L
+    // takes row 16*(c % CPG) + L/4, 16 B chunk L % 4 of the segment.  The
     // row's swizzle (row / 4) % 4 is then (L / 16) % 4 for every copy, so
     // only these per-lane parts live in VGPRs.
-    static_assert(GB == 4 * 1024, "four 1 KiB copies per column group");
     const int lrow = lane >> 2;
     const unsigned k_chunk = (unsigned)((lane & 3) ^ ((lane >> 4) & 3)) * 16;  // bytes
     const unsigned v_chunk = (unsigned)(lane & 3) * 16;
+    // First copy of this wave in a tile (wave-uniform), and whether it copies.
+    const int kcp0 = SPLIT ? wave : wave * NLD;
+    const int vcp0 = SPLIT ? wave - NCP : wave * NLD;
+    const bool kcopies = !SPLIT || wave < NCP;
+    const bool vcopies = !SPLIT || (wave >= NCP && wave < 2 * NCP);
     // Source address = wave-uniform base (scalar registers) + a non-negative
     // 32-bit per-lane byte offset.  Rows past S (last, partial tile) are
     // clamped to row S-1: finite data that the softmax masks out.
@@ -255,49 +268,54 @@ void attn_fwd(AttnArgs a)
     unsigned koff[NLD], voff[NLD];
 #pragma unroll
     for (int n = 0; n < NLD; ++n) {
-        const int cp = wave * NLD + n;
-        const unsigned rowoff = (unsigned)((16 * (cp & 3) + lrow) * rs + (cp >> 2) * 32) * 2;
-        koff[n] = rowoff + k_chunk;
-        voff[n] = rowoff + v_chunk;
+        const int kc = kcopies ? kcp0 + n : 0, vc = vcopies ? vcp0 + n : 0;
+        koff[n] = (unsigned)((16 * (kc % CPG) + lrow) * rs + (kc / CPG) * 32) * 2 + k_chunk;
+        voff[n] = (unsigned)((16 * (vc % CPG) + lrow) * rs + (vc / CPG) * 32) * 2 + v_chunk;
     }
-    auto tile_copy = [&](const uint16_t *src, const unsigned *off, unsigned chunk, int t, lds_u8 *dst) {
-        const int kv0 = t * kBn;
+    auto tile_copy = [&](const uint16_t *src, const unsigned *off, unsigned chunk, int cp0, int t, lds_u8 *dst) {
+        const int kv0 = t * KB;
         const char *base = (const char *)(src + (int64_t)kv0 * rs);
-        if (kv0 + kBn <= S32) {
+        if (kv0 + KB <= S32) {
 #pragma unroll
             for (int n = 0; n < NLD; ++n)
                 __builtin_amdgcn_global_load_lds((gbl_void *)(base + off[n]),
-                                                 (lds_void *)(dst + (wave * NLD + n) * 1024), 16, 0, 0);
+                                                 (lds_void *)(dst + (cp0 + n) * 1024), 16, 0, 0);
         } else {
             asm volatile("");  // a real branch: full tiles keep their precomputed offsets
             const int last = S32 - 1 - kv0;  // last row inside S
 #pragma unroll
             for (int n = 0; n < NLD; ++n) {
-                const int cp = wave * NLD + n;
-                const int row = 16 * (cp & 3) + lrow;
+                const int cp = cp0 + n;
+                const int row = 16 * (cp % CPG) + lrow;
                 const int r = row < last ? row : last;
-                const unsigned o = (unsigned)(r * rs + (cp >> 2) * 32) * 2 + chunk;
+                const unsigned o = (unsigned)(r * rs + (cp / CPG) * 32) * 2 + chunk;
                 __builtin_amdgcn_global_load_lds((gbl_void *)(base + o), (lds_void *)(dst + cp * 1024), 16, 0, 0);
             }
         }
     };
-    auto copy_k = [&](int t, int buf) { tile_copy(kh, koff, k_chunk, t, (lds_u8 *)ks + buf * TILE); };
-    auto copy_v = [&](int t, int buf) { tile_copy(vh, voff, v_chunk, t, (lds_u8 *)vs + buf * TILE); };
+    auto copy_k = [&](int t, int buf) {
+        if (kcopies) tile_copy(kh, koff, k_chunk, kcp0, t, (lds_u8 *)ks + buf * TILE);
+    };
+    auto copy_v = [&](int t, int buf) {
+        if (vcopies) tile_copy(vh, voff, v_chunk, vcp0, t, (lds_u8 *)vs + buf * TILE);
+    };
     // All of this wave's copies have landed; after the barrier every wave's
     // have, and every wave has finished the previous iteration.  A plain
     // s_barrier: reads still in flight (operand prefetch) target other buffers.
     auto sync_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-    // This lane's query row; rows past S (ragged last Q tile) compute on row
-    // S-1 and are not stored.
-    const int64_t s_q = (int64_t)qt * BR + wave * kRowsPerWave + il;
-    const int64_t s_ld = s_q < S ? s_q : S - 1;
-
-    // B operand of S^T = K Q^T: lane holds Q[s][16kk + 8g .. +7].
-    u32x4 qf[KK];
+    // This lane's query row in each row block; rows past S (ragged last Q
+    // tile) compute on row S-1 and are not stored.
+    int64_t s_q[RB];
+    u32x4 qf[RB][KK];  // B operand of S^T = K Q^T: lane holds Q[s][16kk + 8g .. +7]
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-        qf[kk] = *(const u32x4 *)(qh + s_ld * rs + 16 * kk + 8 * g);
+    for (int rb = 0; rb < RB; ++rb) {
+        s_q[rb] = (int64_t)qt * BR + wave * RW + rb * 32 + il;
+        const int64_t s_ld = s_q[rb] < S ? s_q[rb] : S - 1;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qf[rb][kk] = *(const u32x4 *)(qh + s_ld * rs + 16 * kk + 8 * g);
+    }
 
     // Per-lane LDS byte addresses of the operand reads; buffers and blocks
     // are instruction offsets.
@@ -313,15 +331,17 @@ void attn_fwd(AttnArgs a)
     const unsigned kb0 = (unsigned)(uintptr_t)(lds_u8 *)ks + il * 64 + (((0 + g) ^ ((il >> 2) & 3)) * 16);
     const unsigned kb1 = (unsigned)(uintptr_t)(lds_u8 *)ks + il * 64 + (((2 + g) ^ ((il >> 2) & 3)) * 16);
     const unsigned vb = (unsigned)(uintptr_t)(lds_u8 *)vs + (4 * g + (i16 >> 2)) * 64 + (16 * half + 4 * (i16 & 3)) * 2;
-    f32x16 oacc[DB];
+    f32x16 oacc[RB][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
     // S^T of the K tile in buffer kbuf (outside the steady loop).
-    auto qk = [&](int kbuf, f32x16 (&s)[kNB]) {
+    auto qk = [&](int kbuf, f32x16 (&s)[RB][KNB]) {
         const unsigned ko = kbuf * TILE;
-        static_for<kNB>([&](auto jc) {
+        static_for<KNB>([&](auto jc) {
             constexpr int jb = decltype(jc)::value;
             u32x4 kf[KK];
             static_for<KK>([&](auto kc) {
@@ -329,19 +349,22 @@ void attn_fwd(AttnArgs a)
                 kf[kk] = lds_b128<(kk >> 1) * GB + jb * 32 * 64>(((kk & 1) ? kb1 : kb0) + ko);
             });
             const f32x16 zero = {};
-            s[jb] = zero;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) s[rb][jb] = zero;
             static_for<KK>([&](auto kc) {
                 constexpr int kk = decltype(kc)::value;
                 lgkm_wait<KK - 1 - kk>(kf[kk]);
-                s[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf[kk]),
-                                                                __builtin_bit_cast(bf16x8, qf[kk]), s[jb], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    s[rb][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, kf[kk]), __builtin_bit_cast(bf16x8, qf[rb][kk]), s[rb][jb], 0, 0, 0);
             });
         });
     };
     // O^T += V^T P^T for the V tile in buffer vbuf (outside the steady loop).
-    auto pv = [&](int vbuf, const u32x4 (&pb)[2 * kNB]) {
+    auto pv = [&](int vbuf, const u32x4 (&pb)[RB][2 * KNB]) {
         const unsigned vo = vbuf * TILE;
-        static_for<2 * kNB>([&](auto ccc) {
+        static_for<2 * KNB>([&](auto ccc) {
             constexpr int cc = decltype(ccc)::value;
             u32x4 af[DB];
             static_for<DB>([&](auto dbc) {
@@ -354,144 +377,169 @@ void attn_fwd(AttnArgs a)
             static_for<DB>([&](auto dbc) {
                 constexpr int db = decltype(dbc)::value;
                 lgkm_wait<2 * (DB - 1 - db)>(af[db]);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, af[db]), __builtin_bit_cast(bf16x8, pb[cc]), oacc[db], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, af[db]), __builtin_bit_cast(bf16x8, pb[rb][cc]), oacc[rb][db], 0, 0, 0);
             });
         });
     };
 
-    // ---- online softmax in the log2 domain.  m_run is the running max of
-    // this row's scaled scores.  It is only a stabiliser: it is raised when a
-    // tile's max exceeds it by more than 8 (a factor 256), so P stays below
-    // 2^8 and O rarely needs rescaling; O / l comes out the same for any
-    // choice of it.  l_run is this lane's part of the row sum, taken over the
-    // same bf16-rounded P that feeds the PV product.
+    // ---- online softmax in the log2 domain, per row block.  m_run is the
+    // running max of this row's scaled scores.  It is only a stabiliser: it
+    // is raised when a tile's max exceeds it by more than 8 (a factor 256), so
+    // P stays below 2^8 and O rarely needs rescaling; O / l comes out the same
+    // for any choice of it.  l_run is this lane's part of the row sum, taken
+    // over the same bf16-rounded P that feeds the PV product.
     const float c = a.scale_log2;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    float m_run[RB], l_run[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+    }
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    // Raise decision for a tile whose scaled max is mt.  Returns true (for
-    // the whole wave) when some row raised its max; O must then be multiplied
-    // by alpha once the previous tile's PV product has been added.
-    auto raise_max = [&](float mt, float &alpha) -> bool {
-        const bool raise = mt > m_run + 8.0f;  // same in both lanes of a row
-        const float m_new = raise ? mt : m_run;
-        alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // exactly 1 when kept, 0 at the start
-        m_run = m_new;
-        l_run *= alpha;
-        return __builtin_amdgcn_ballot_w64(raise) != 0;
+    // Raise decision for row block rb and a tile whose scaled max is mt.
+    // Returns this lane's decision; O must be multiplied by alpha once the
+    // previous tile's PV product has been added.
+    auto raise_max = [&](int rb, float mt, float &alpha) -> bool {
+        const bool raise = mt > m_run[rb] + 8.0f;  // same in both lanes of a row
+        const float m_new = raise ? mt : m_run[rb];
+        alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);  // exactly 1 when kept, 0 at the start
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+        return raise;
     };
-    auto softmax_max = [&](f32x16 (&s)[kNB], int valid, float &alpha) -> bool {
-        if (valid < kBn) {
+    // Tile max and raise for every row block; true (for the whole wave) when
+    // some row raised its max.
+    auto softmax_max = [&](f32x16 (&s)[RB][KNB], int valid, float (&alpha)[RB]) -> bool {
+        bool raised = false;
 #pragma unroll
-            for (int jb = 0; jb < kNB; ++jb)
+        for (int rb = 0; rb < RB; ++rb) {
+            if (valid < KB) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= valid) s[jb][r] = -INFINITY;
-        }
-        // two independent chains keep the max reduction short
-        float m0 = fmaxf(s[0][0], s[0][1]), m1 = fmaxf(s[0][2], s[0][3]);
+                for (int jb = 0; jb < KNB; ++jb)
 #pragma unroll
-        for (int jb = 0; jb < kNB; ++jb)
-#pragma unroll
-            for (int r = (jb == 0 ? 4 : 0); r < 16; r += 2) {
-                m0 = fmaxf(m0, s[jb][r]);
-                m1 = fmaxf(m1, s[jb][r + 1]);
+                    for (int r = 0; r < 16; ++r)
+                        if (jb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= valid) s[rb][jb][r] = -INFINITY;
             }
-        return raise_max(row_max(fmaxf(m0, m1)) * c, alpha);
+            // two independent chains keep the max reduction short
+            float m0 = fmaxf(s[rb][0][0], s[rb][0][1]), m1 = fmaxf(s[rb][0][2], s[rb][0][3]);
+#pragma unroll
+            for (int jb = 0; jb < KNB; ++jb)
+#pragma unroll
+                for (int r = (jb == 0 ? 4 : 0); r < 16; r += 2) {
+                    m0 = fmaxf(m0, s[rb][jb][r]);
+                    m1 = fmaxf(m1, s[rb][jb][r + 1]);
+                }
+            raised |= raise_max(rb, row_max(fmaxf(m0, m1)) * c, alpha[rb]);
+        }
+        return __builtin_amdgcn_ballot_w64(raised) != 0;
     };
-    // P for two neighbouring keys of chunk cc, rounded to bf16 and packed as
-    // the B operand of the PV product; the row sum takes the rounded values.
-    auto exp_pair = [&](const f32x16 (&s)[kNB], u32x4 (&pb)[2 * kNB], int cc, int e2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * e2], c, -m_run));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[cc >> 1][8 * (cc & 1) + 2 * e2 + 1], c, -m_run));
+    // P for two neighbouring keys of chunk cc of row block rb, rounded to
+    // bf16 and packed as the B operand of the PV product; the row sum takes
+    // the rounded values.
+    auto exp_pair = [&](const f32x16 (&s)[RB][KNB], u32x4 (&pb)[RB][2 * KNB], int rb, int cc, int e2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][cc >> 1][8 * (cc & 1) + 2 * e2], c, -m_run[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][cc >> 1][8 * (cc & 1) + 2 * e2 + 1], c, -m_run[rb]));
         f32x2 f = {p0, p1};
         const bf16x2 hb = __builtin_convertvector(f, bf16x2);
-        pb[cc][e2] = __builtin_bit_cast(unsigned, hb);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(hb, ones, l_run, false);
+        pb[rb][cc][e2] = __builtin_bit_cast(unsigned, hb);
+        l_run[rb] = __builtin_amdgcn_fdot2_f32_bf16(hb, ones, l_run[rb], false);
         // Pin both results here in program order: otherwise the compiler
         // sinks the whole exp work towards its first use (the next
         // iteration's PV MFMAs) and runs it as one block without MFMA overlap.
-        asm volatile("" : "+v"(pb[cc][e2]), "+v"(l_run));
+        asm volatile("" : "+v"(pb[rb][cc][e2]), "+v"(l_run[rb]));
     };
-    auto softmax_exp = [&](const f32x16 (&s)[kNB], u32x4 (&pb)[2 * kNB]) {
+    auto softmax_exp = [&](const f32x16 (&s)[RB][KNB], u32x4 (&pb)[RB][2 * KNB]) {
 #pragma unroll
-        for (int cc = 0; cc < 2 * kNB; ++cc)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) exp_pair(s, pb, cc, e2);
+            for (int cc = 0; cc < 2 * KNB; ++cc)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) exp_pair(s, pb, rb, cc, e2);
     };
-    auto rescale_o = [&](float alpha) {
+    auto rescale_o = [&](const float (&alpha)[RB]) {
         asm volatile("");  // keeps this off the common path (no if-conversion)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha[rb];
     };
 
     // ---- software pipeline over KV tiles.  Iteration t: softmax of S_t
     // interleaves with the MFMAs of PV_{t-1} and of S_{t+1}.  Tile copies
-    // run one iteration ahead through a three-buffer ring (iteration t
-    // copies K_{t+3} and V_{t+1}), so the operand reads of the next
-    // iteration's first MFMAs can be issued before its barrier.
-    const int ntiles = (int)((S + kBn - 1) / kBn);
-    const int valid_last = (int)(S - (int64_t)(ntiles - 1) * kBn);
-    f32x16 s_cur[kNB], s_nxt[kNB];         // S_t, S_{t+1}
-    u32x4 p_cur[2 * kNB], p_prv[2 * kNB];  // packed P_t, P_{t-1}
+    // run ahead through three-buffer rings (iteration t copies K_{t+3} and
+    // V_{t+1}), so the operand reads of the next iteration's first MFMAs can
+    // be issued before its barrier.
+    const int ntiles = (int)((S + KB - 1) / KB);
+    const int valid_last = (int)(S - (int64_t)(ntiles - 1) * KB);
+    f32x16 s_cur[RB][KNB], s_nxt[RB][KNB];         // S_t, S_{t+1}
+    u32x4 p_cur[RB][2 * KNB], p_prv[RB][2 * KNB];  // packed P_t, P_{t-1}
     auto rotate = [&]() {
 #pragma unroll
-        for (int jb = 0; jb < kNB; ++jb) s_cur[jb] = s_nxt[jb];
+        for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int cc = 0; cc < 2 * kNB; ++cc) p_prv[cc] = p_cur[cc];
+            for (int jb = 0; jb < KNB; ++jb) s_cur[rb][jb] = s_nxt[rb][jb];
+#pragma unroll
+            for (int cc = 0; cc < 2 * KNB; ++cc) p_prv[rb][cc] = p_cur[rb][cc];
+        }
     };
 
-    // Steady iteration with an explicit issue order.  Slot m issues the LDS
-    // reads for MFMA m + kPF (of the next iteration near the end), MFMA m,
-    // and a fixed slice of the softmax VALU work; scheduling fences keep
-    // the compiler from gathering the VALU work into one block.
-    //   MFMA order: PV_{t-1} (chunk cc, block db), then S_{t+1} (block jb,
-    //   k-step kk).  VALU order: tile max of S_t in NMX slots, then the
+    // Steady iteration with an explicit issue order.  The MFMAs come in
+    // groups of RB that share one LDS operand fragment (one MFMA per row
+    // block).  Slot m issues MFMA m; the first slot of fragment f's group
+    // also issues the LDS reads for fragment f + kPF (of the next iteration
+    // near the end) and waits for fragment f; every slot carries a fixed
+    // slice of the softmax VALU work, and scheduling fences keep the
+    // compiler from gathering it into one block.
+    //   Fragment order: PV_{t-1} (chunk cc, block db), then S_{t+1} (block
+    //   jb, k-step kk).  VALU order: tile max of S_t in NMX slots, then the
     //   raise step, then EPS exp pairs per slot.
-    constexpr int NPV = 2 * kNB * DB;
-    constexpr int NS = kNB * KK;
-    constexpr int NM = NPV + NS;
-    constexpr int NMX = 2 * kNB;  // max slots, 8 values each
-    constexpr int NEX = 8 * kNB;  // exp pairs
+    constexpr int NPV = 2 * KNB * DB;  // PV fragments
+    constexpr int NS = KNB * KK;       // S fragments
+    constexpr int NF = NPV + NS;       // fragments per iteration
+    constexpr int NM = NF * RB;        // MFMAs (slots) per iteration
+    constexpr int NMX = 2 * KNB * RB;  // max slots, 8 values each
+    constexpr int NEX = 8 * KNB * RB;  // exp pairs
     constexpr int EPS = (NEX + (NM - NMX - 1) - 1) / (NM - NMX - 1);
     static_assert(NM > NMX + 1, "no slots left for the exp pairs");
     static_assert(kPF <= NPV, "the prefetch crossing into the next iteration reads V fragments");
-    constexpr int NRD_PV = 2, NRD_S = 1;  // LDS reads per MFMA fragment
-    // reads issued after fragment m's and before MFMA m (fragments m+1 .. m+kPF,
-    // those past NM belonging to the next iteration)
-    auto after = [](int m) constexpr {
+    constexpr int NRD_PV = 2, NRD_S = 1;  // LDS reads per fragment
+    // reads issued after fragment f's and before its first MFMA (fragments
+    // f+1 .. f+kPF, those past NF belonging to the next iteration)
+    auto after = [](int f) constexpr {
         int n = 0;
-        for (int j = m + 1; j <= m + kPF; ++j) n += (j % NM) < NPV ? NRD_PV : NRD_S;
+        for (int j = f + 1; j <= f + kPF; ++j) n += (j % NF) < NPV ? NRD_PV : NRD_S;
         return n;
     };
-    // fragment m of an iteration whose V_{t-1} / K_{t+1} sit in buffers VBUF / KBUF
-    auto load_frag = [&](auto mc, auto vbufc, auto kbufc, u32x4 &dst) {
-        constexpr int m = decltype(mc)::value;
+    // fragment f of an iteration whose V_{t-1} / K_{t+1} sit in buffers VBUF / KBUF
+    auto load_frag = [&](auto fc, auto vbufc, auto kbufc, u32x4 &dst) {
+        constexpr int f = decltype(fc)::value;
         constexpr int VO = decltype(vbufc)::value * TILE, KO = decltype(kbufc)::value * TILE;
-        if constexpr (m < NPV) {
-            constexpr int cc = m / DB, db = m % DB;
+        if constexpr (f < NPV) {
+            constexpr int cc = f / DB, db = f % DB;
             constexpr int off = VO + db * GB + 16 * cc * 64;
             const u32x2 a1 = lds_tr16<off>(vb);
             const u32x2 a2 = lds_tr16<off + 8 * 64>(vb);
             dst = u32x4{a1[0], a1[1], a2[0], a2[1]};
         } else {
-            constexpr int q = m - NPV, jb = q / KK, kk = q % KK;
+            constexpr int q = f - NPV, jb = q / KK, kk = q % KK;
             constexpr int off = KO + (kk >> 1) * GB + jb * 32 * 64;
             dst = lds_b128<off>((kk & 1) ? kb1 : kb0);
         }
     };
-    // Operand fragments in flight, carried across iterations: fragment m of
-    // every iteration sits in fr[m % FR], so the ring size must divide NM.
+    // Operand fragments in flight, carried across iterations: fragment f of
+    // every iteration sits in fr[f % FR], so the ring size must divide NF.
     constexpr int FR = 4;
-    static_assert(FR > kPF && NM % FR == 0 && FR == 4, "fragment ring");
+    static_assert(FR > kPF && NF % FR == 0 && FR == 4, "fragment ring");
     u32x4 fr[FR] = {};
     auto steady = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;  // t % 3
         using VB = std::integral_constant<int, (P + 2) % 3>;   // V_{t-1}
-        using KB = std::integral_constant<int, (P + 1) % 3>;   // K_{t+1}
+        using KB_ = std::integral_constant<int, (P + 1) % 3>;  // K_{t+1}
         using VBn = std::integral_constant<int, P>;            // V_t: next iteration
         using KBn = std::integral_constant<int, (P + 2) % 3>;  // K_{t+2}: next iteration
         // K_{t+2} and V_t (copied during iteration t-1) have landed and
@@ -501,52 +549,63 @@ void attn_fwd(AttnArgs a)
         if (t + 3 < ntiles) copy_k(t + 3, P);
         copy_v(t + 1, (P + 1) % 3);
         float mx[NMX];
-        float alpha = 1.f;
+        float alpha[RB];
         bool any = false;
         static_for<NM>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
-            if constexpr (m + kPF < NM)
-                load_frag(std::integral_constant<int, m + kPF>(), VB(), KB(), fr[(m + kPF) % FR]);
-            else
-                load_frag(std::integral_constant<int, m + kPF - NM>(), VBn(), KBn(), fr[(m + kPF - NM) % FR]);
-            u32x4 &f = fr[m % FR];
-            lgkm_wait<after(m)>(f);
-            if constexpr (m < NPV) {
-                constexpr int cc = m / DB, db = m % DB;
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, f), __builtin_bit_cast(bf16x8, p_prv[cc]), oacc[db], 0, 0, 0);
+            constexpr int f = m / RB, r = m % RB;  // fragment, row block
+            if constexpr (r == 0) {
+                if constexpr (f + kPF < NF)
+                    load_frag(std::integral_constant<int, f + kPF>(), VB(), KB_(), fr[(f + kPF) % FR]);
+                else
+                    load_frag(std::integral_constant<int, f + kPF - NF>(), VBn(), KBn(), fr[(f + kPF - NF) % FR]);
+                lgkm_wait<after(f)>(fr[f % FR]);
+            }
+            u32x4 &fg = fr[f % FR];
+            if constexpr (f < NPV) {
+                constexpr int cc = f / DB, db = f % DB;
+                oacc[r][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, fg), __builtin_bit_cast(bf16x8, p_prv[r][cc]), oacc[r][db], 0, 0, 0);
             } else {
-                constexpr int q = m - NPV, jb = q / KK, kk = q % KK;
+                constexpr int q = f - NPV, jb = q / KK, kk = q % KK;
                 if constexpr (kk == 0) {
                     const f32x16 zero = {};
-                    s_nxt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, f), __builtin_bit_cast(bf16x8, qf[kk]), zero, 0, 0, 0);
+                    s_nxt[r][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fg), __builtin_bit_cast(bf16x8, qf[r][kk]), zero, 0, 0, 0);
                 } else {
-                    s_nxt[jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, f), __builtin_bit_cast(bf16x8, qf[kk]), s_nxt[jb], 0, 0, 0);
+                    s_nxt[r][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fg), __builtin_bit_cast(bf16x8, qf[r][kk]), s_nxt[r][jb], 0, 0, 0);
                 }
             }
             // softmax slice of slot m
             if constexpr (m < NMX) {
-                // one running max over the tile, two new values per v_max3
-                constexpr int jb = m >> 1, r0 = (m & 1) * 8;
-                float r;
-                if constexpr (m == 0)
-                    r = fmaxf(fmaxf(s_cur[jb][0], s_cur[jb][1]), s_cur[jb][2]);
+                // one running max per row block, two new values per v_max3
+                constexpr int mrb = m / (2 * KNB), ms = m % (2 * KNB);
+                constexpr int jb = ms >> 1, r0 = (ms & 1) * 8;
+                float v;
+                if constexpr (ms == 0)
+                    v = fmaxf(fmaxf(s_cur[mrb][jb][0], s_cur[mrb][jb][1]), s_cur[mrb][jb][2]);
                 else
-                    r = fmaxf(fmaxf(mx[m - 1], s_cur[jb][r0]), s_cur[jb][r0 + 1]);
-                constexpr int i0 = m == 0 ? 3 : 2;
+                    v = fmaxf(fmaxf(mx[m - 1], s_cur[mrb][jb][r0]), s_cur[mrb][jb][r0 + 1]);
+                constexpr int i0 = ms == 0 ? 3 : 2;
 #pragma unroll
-                for (int i = i0; i + 1 < 8; i += 2) r = fmaxf(fmaxf(r, s_cur[jb][r0 + i]), s_cur[jb][r0 + i + 1]);
-                if constexpr (i0 == 3) r = fmaxf(r, s_cur[jb][r0 + 7]);
-                mx[m] = r;
+                for (int i = i0; i + 1 < 8; i += 2) v = fmaxf(fmaxf(v, s_cur[mrb][jb][r0 + i]), s_cur[mrb][jb][r0 + i + 1]);
+                if constexpr (i0 == 3) v = fmaxf(v, s_cur[mrb][jb][r0 + 7]);
+                mx[m] = v;
                 asm volatile("" : "+v"(mx[m]));
             } else if constexpr (m == NMX) {
-                any = raise_max(row_max(mx[NMX - 1]) * c, alpha);
+                bool raised = false;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    raised |= raise_max(rb, row_max(mx[(rb + 1) * 2 * KNB - 1]) * c, alpha[rb]);
+                any = __builtin_amdgcn_ballot_w64(raised) != 0;
             } else {
                 static_for<EPS>([&](auto xc) {
                     constexpr int e = (m - NMX - 1) * EPS + decltype(xc)::value;
-                    if constexpr (e < NEX) exp_pair(s_cur, p_cur, e >> 2, e & 3);
+                    if constexpr (e < NEX) {
+                        constexpr int erb = e / (8 * KNB), w = e % (8 * KNB);
+                        exp_pair(s_cur, p_cur, erb, w >> 2, w & 3);
+                    }
                 });
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -569,8 +628,8 @@ void attn_fwd(AttnArgs a)
     qk(0, s_cur);
 
     // iteration 0: softmax S_0 -> P_0 with S_1
-    float alpha0;
-    softmax_max(s_cur, ntiles == 1 ? valid_last : kBn, alpha0);
+    float alpha0[RB];
+    softmax_max(s_cur, ntiles == 1 ? valid_last : KB, alpha0);
     if (ntiles == 1) {
         softmax_exp(s_cur, p_cur);
         pv(0, p_cur);
@@ -584,9 +643,9 @@ void attn_fwd(AttnArgs a)
         copy_v(1, 1);
         // operands of the first steady iteration (V_0 and K_2, landed)
         if (ntiles > 2)
-            static_for<kPF>([&](auto mc) {
-                load_frag(mc, std::integral_constant<int, 0>(), std::integral_constant<int, 2>(),
-                          fr[decltype(mc)::value % FR]);
+            static_for<kPF>([&](auto fc) {
+                load_frag(fc, std::integral_constant<int, 0>(), std::integral_constant<int, 2>(),
+                          fr[decltype(fc)::value % FR]);
             });
         // steady iterations t = 1 .. ntiles-2, unrolled by three so that
         // every buffer is fixed at compile time.
@@ -612,7 +671,7 @@ void attn_fwd(AttnArgs a)
         // registers stay reserved (tied to this wait) until they land.
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fr[0]), "+v"(fr[1]), "+v"(fr[2]), "+v"(fr[3])::"memory");
         sync_all();
-        float alpha;
+        float alpha[RB];
         const bool any = softmax_max(s_cur, valid_last, alpha);
         pv((t + 2) % 3, p_prv);
         softmax_exp(s_cur, p_cur);
@@ -620,30 +679,34 @@ void attn_fwd(AttnArgs a)
         pv(t % 3, p_cur);
     }
 
-    // ---- epilogue: normalise and store this lane's half of its row straight
-    // into the destination slot (region p, row i, head g0 + h).
-    const float lt = row_sum(l_run);
-    const float inv = 1.0f / lt;
+    // ---- epilogue: normalise and store this lane's half of each of its
+    // rows straight into the destination slot (region p, row i, head g0 + h).
+    float inv[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) inv[rb] = 1.0f / row_sum(l_run[rb]);
     uint64_t tr_sb = 0;
     if constexpr (TRACE) {
         __syncthreads();
         tr_sb = __builtin_amdgcn_s_memrealtime();
     }
-    if (s_q < S) {
-        const Placement &o = a.out;
-        const int64_t p = s_q / o.region_rows;
-        const int64_t i = s_q - p * o.region_rows;
-        uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + o.head0 + h) * D;
-        // O^T element r of block db is column db*32 + 8(r/4) + 4g + r%4.
+    const Placement &o = a.out;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+        if (s_q[rb] < S) {
+            const int64_t p = s_q[rb] / o.region_rows;
+            const int64_t i = s_q[rb] - p * o.region_rows;
+            uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + o.head0 + h) * D;
+            // O^T element r of block db is column db*32 + 8(r/4) + 4g + r%4.
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                u32x2 w;
-                w[0] = pack_bf16(oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv);
-                w[1] = pack_bf16(oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv);
-                *(u32x2 *)(dst + db * 32 + 8 * q4 + 4 * g) = w;
-            }
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    u32x2 w;
+                    w[0] = pack_bf16(oacc[rb][db][4 * q4] * inv[rb], oacc[rb][db][4 * q4 + 1] * inv[rb]);
+                    w[1] = pack_bf16(oacc[rb][db][4 * q4 + 2] * inv[rb], oacc[rb][db][4 * q4 + 3] * inv[rb]);
+                    *(u32x2 *)(dst + db * 32 + 8 * q4 + 4 * g) = w;
+                }
+        }
     }
     if constexpr (TRACE) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -662,10 +725,11 @@ void attn_fwd(AttnArgs a)
 
 // Epilogue stores alone: the attention kernel's grid, work-unit order and
 // per-lane store pattern (8-byte chunks of one row per lane, placed by the
-// same Placement arithmetic), with a closed-form value instead of attention
-// output: element (s, head g, column c) gets bf16 bits (7s + 13g + 3c) & 0x3FFF
-// (finite, positive).  Measures what the destination layout sustains.
-template <int D, int NW>
+// same Placement arithmetic, RB row blocks per wave), with a closed-form
+// value instead of attention output: element (s, head g, column c) gets bf16
+// bits (7s + 13g + 3c) & 0x3FFF (finite, positive).  Measures what the
+// destination layout sustains.
+template <int D, int NW, int RB>
 __global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S, int32_t Hl, int32_t n_qtiles,
                                                          int32_t n_units)
 {
@@ -677,23 +741,26 @@ __global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S,
     const int bh = unit / n_qtiles;
     const int h = bh % Hl;
     const int64_t b = bh / Hl;
-    const int64_t s_q = (int64_t)qt * (kRowsPerWave * NW) + wave * kRowsPerWave + il;
-    if (s_q >= S) return;
-    const int64_t p = s_q / o.region_rows;
-    const int64_t i = s_q - p * o.region_rows;
-    const int64_t gh = o.head0 + h;
-    uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + gh) * D;
-    const unsigned base = (unsigned)(7 * s_q + 13 * gh);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int rb = 0; rb < RB; ++rb) {
+        const int64_t s_q = (int64_t)qt * (32 * RB * NW) + wave * (32 * RB) + rb * 32 + il;
+        if (s_q >= S) continue;
+        const int64_t p = s_q / o.region_rows;
+        const int64_t i = s_q - p * o.region_rows;
+        const int64_t gh = o.head0 + h;
+        uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + gh) * D;
+        const unsigned base = (unsigned)(7 * s_q + 13 * gh);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const unsigned c = db * 32 + 8 * q4 + 4 * g;
-            u32x2 w;
-            w[0] = ((base + 3 * c) & 0x3FFFu) | (((base + 3 * (c + 1)) & 0x3FFFu) << 16);
-            w[1] = ((base + 3 * (c + 2)) & 0x3FFFu) | (((base + 3 * (c + 3)) & 0x3FFFu) << 16);
-            *(u32x2 *)(dst + c) = w;
-        }
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const unsigned c = db * 32 + 8 * q4 + 4 * g;
+                u32x2 w;
+                w[0] = ((base + 3 * c) & 0x3FFFu) | (((base + 3 * (c + 1)) & 0x3FFFu) << 16);
+                w[1] = ((base + 3 * (c + 2)) & 0x3FFFu) | (((base + 3 * (c + 3)) & 0x3FFFu) << 16);
+                *(u32x2 *)(dst + c) = w;
+            }
+    }
 }
 
 // Serial All-to-All: each thread copies one 16-byte chunk.  For a fixed
@@ -736,21 +803,38 @@ __global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chun
     *(u32x4 *)(dst + (int64_t)c * 8) = *(const u32x4 *)src;
 }
 
-// Waves per workgroup for a shape: 8 (one K/V tile per 256 query rows) when
-// that still gives at least half a workgroup per CU, else 4.
-int waves_for(int64_t B, int64_t S, int64_t Hl, int d)
+// Launch shape of the attention kernel for a problem: waves per workgroup,
+// 32-row blocks per wave, keys per K/V tile.  8 waves (one K/V tile per 256
+// query rows) when that still gives at least half a workgroup per CU, else
+// 4.  For d = 64 with at least 128 units of 512 rows, 8 waves of two row
+// blocks each on 32-key tiles (each LDS operand fragment feeds two MFMAs).
+struct LaunchShape {
+    int nw, rb, kb;
+    int rows() const { return 32 * rb * nw; }
+};
+
+LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    (void)d;
-    const int64_t units8 = B * Hl * ((S + 8 * kRowsPerWave - 1) / (8 * kRowsPerWave));
-    return units8 >= 128 ? 8 : 4;
+    const auto units = [&](int rows) { return B * Hl * ((S + rows - 1) / rows); };
+    if (d == 64 && units(512) >= 128) return {8, 2, 32};
+    return units(256) >= 128 ? LaunchShape{8, 1, 64} : LaunchShape{4, 1, 64};
+}
+
+template <bool TRACE>
+const void *attention_kernel(int d, const LaunchShape &ls)
+{
+    if (d == 128)
+        return ls.nw == 8 ? (const void *)attn_fwd<128, 8, 1, 64, TRACE> : (const void *)attn_fwd<128, 4, 1, 64, TRACE>;
+    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, TRACE>;
+    return ls.nw == 8 ? (const void *)attn_fwd<64, 8, 1, 64, TRACE> : (const void *)attn_fwd<64, 4, 1, 64, TRACE>;
 }
 
 }  // namespace
 
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const int nw = waves_for(B, S, Hl, d);
-    return B * Hl * ((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
+    const LaunchShape ls = launch_shape(B, S, Hl, d);
+    return B * Hl * ((S + ls.rows() - 1) / ls.rows());
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -758,7 +842,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             int d, float scale, const Placement &out, hipStream_t stream,
                             uint64_t *trace)
 {
-    const int nw = waves_for(B, S, Hl, d);
+    const LaunchShape ls = launch_shape(B, S, Hl, d);
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -768,34 +852,33 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.Hl = (int32_t)Hl;
     a.in_heads = (int32_t)in_heads;
     a.in_head0 = (int32_t)in_head0;
-    a.n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
+    a.n_qtiles = (int32_t)((S + ls.rows() - 1) / ls.rows());
     a.n_units = (int32_t)attention_units(B, S, Hl, d);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.trace = trace;
     void *args[] = {&a};
-    const void *fn;
-    if (trace)
-        fn = d == 128 ? (nw == 8 ? (const void *)attn_fwd<128, 8, true> : (const void *)attn_fwd<128, 4, true>)
-                      : (nw == 8 ? (const void *)attn_fwd<64, 8, true> : (const void *)attn_fwd<64, 4, true>);
-    else
-        fn = d == 128 ? (nw == 8 ? (const void *)attn_fwd<128, 8, false> : (const void *)attn_fwd<128, 4, false>)
-                      : (nw == 8 ? (const void *)attn_fwd<64, 8, false> : (const void *)attn_fwd<64, 4, false>);
-    return hipLaunchKernel(fn, dim3(a.n_units), dim3(64 * nw), args, 0, stream);
+    const void *fn = trace ? attention_kernel<true>(d, ls) : attention_kernel<false>(d, ls);
+    return hipLaunchKernel(fn, dim3(a.n_units), dim3(64 * ls.nw), args, 0, stream);
 }
 
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
                                 hipStream_t stream)
 {
-    const int nw = waves_for(B, S, Hl, d);
+    const LaunchShape ls = launch_shape(B, S, Hl, d);
     Placement o = out;
     int64_t S64 = S;
     int32_t Hl32 = (int32_t)Hl;
-    int32_t n_qtiles = (int32_t)((S + nw * kRowsPerWave - 1) / (nw * kRowsPerWave));
+    int32_t n_qtiles = (int32_t)((S + ls.rows() - 1) / ls.rows());
     int32_t n_units = (int32_t)attention_units(B, S, Hl, d);
     void *args[] = {&o, &S64, &Hl32, &n_qtiles, &n_units};
-    const void *fn = d == 128 ? (nw == 8 ? (const void *)epilogue_only<128, 8> : (const void *)epilogue_only<128, 4>)
-                              : (nw == 8 ? (const void *)epilogue_only<64, 8> : (const void *)epilogue_only<64, 4>);
-    return hipLaunchKernel(fn, dim3(n_units), dim3(64 * nw), args, 0, stream);
+    const void *fn;
+    if (d == 128)
+        fn = ls.nw == 8 ? (const void *)epilogue_only<128, 8, 1> : (const void *)epilogue_only<128, 4, 1>;
+    else if (ls.rb == 2)
+        fn = (const void *)epilogue_only<64, 8, 2>;
+    else
+        fn = ls.nw == 8 ? (const void *)epilogue_only<64, 8, 1> : (const void *)epilogue_only<64, 4, 1>;
+    return hipLaunchKernel(fn, dim3(n_units), dim3(64 * ls.nw), args, 0, stream);
 }
 
 hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t Hl, int d,

@@ -76,6 +76,9 @@ SMALL = [
     # enough work units for the 8-wave, 256-row workgroups, with ragged tails
     (1, 520, 64, 1, 0, 128, 9),    # 520 = 2 full 256-row tiles + 8 rows; 8 KV tiles + 8 keys
     (2, 1030, 32, 2, 1, 64, 10),   # d = 64, regions of 515 rows
+    # d = 64 with enough units of 512 rows for two row blocks per wave on
+    # 32-key tiles: 1100 = 34 tiles + 12 keys, 2 units of 512 rows + 76
+    (2, 1100, 64, 2, 1, 64, 13),
 ]
 
 
