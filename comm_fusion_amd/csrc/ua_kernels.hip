@@ -10,9 +10,11 @@
 // output-tile owner issues the exchange stores itself, then moves on).
 //
 // Design for CDNA4, not a translation of the pages' FlashAttention-3/4:
-//  * a workgroup of NW wave64s (8, or 4 for small problems) owns 32*NW query
-//    rows of one (batch, local head); each wave owns 32 rows.  All waves
-//    share each K/V tile, so a tile crosses L2 -> LDS once per 32*NW rows;
+//  * a workgroup of NW wave64s (8, or 4 for small problems) owns 32*RB*NW
+//    query rows of one (batch, local head); each wave owns RB blocks of 32
+//    rows (RB = 2 for d = 64, where the registers allow it: each K or V
+//    fragment read from LDS then feeds two MFMAs).  All waves share each
+//    K/V tile, so a tile crosses L2 -> LDS once per 32*RB*NW rows;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K streams from LDS as the A operand and the
 //    wave's Q rows stay in VGPRs as the B operand.  The accumulator layout
@@ -22,7 +24,7 @@
 //  * P^T is fed from those registers (rounded to bf16) as the B operand of
 //    O^T += V^T P^T; V^T comes from the key-major V tile through the gfx950
 //    transposing LDS read ds_read_b64_tr_b16;
-//  * K and V tiles (64 keys) go global -> LDS with global_load_lds_dwordx4
+//  * K and V tiles (64 keys; 32 with RB = 2) go global -> LDS with global_load_lds_dwordx4
 //    (no VGPR staging), through a ring of three buffers, one tile ahead;
 //    the operand reads of an iteration's first MFMAs are issued before its
 //    barrier, at the end of the previous iteration;
