@@ -254,6 +254,7 @@ def traced_call(ua, torch, q, k, v, w, dest) -> dict:
     life_us = (t[:, 2] - t[:, 0]) / 100.0
     unit_bytes = w.out_bytes / n                    # mean bytes a work unit stores
     ok = span_us > 0
+    unit_mhz = t[:, 3] / np.maximum(life_us, 1e-3)   # cycles per us = MHz
     return {
         "trace_work_units": n,
         "epilogue_span_us_mean": round(float(span_us.mean()), 3),
@@ -261,6 +262,8 @@ def traced_call(ua, torch, q, k, v, w, dest) -> dict:
         "epilogue_unit_GBs_mean": round(float((unit_bytes / (span_us[ok] * 1e-6)).mean() / 1e9), 1) if ok.any() else None,
         "epilogue_share_of_unit_time": round(float(span_us.sum() / life_us.sum()), 4),
         "sclk_mhz_trace": round(float(t[:, 3].sum() / (life_us.sum() * 1e-6) / 1e6), 1),
+        # spread of the per-unit clocks (DVFS within the launch)
+        "sclk_mhz_trace_p10_p90": [round(float(np.percentile(unit_mhz, q)), 1) for q in (10, 90)],
     }
 
 
