@@ -193,6 +193,30 @@ def test_wide_rows_many_heads():
     _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, "wide rows")
 
 
+@pytest.mark.parametrize("B,S,H,P,rank,d", [
+    (1, 1, 128, 1, 0, 64),     # one key and one query per head, 128 heads: two-row-block d = 64 launch
+    (1, 2, 256, 2, 0, 64),     # S = P
+    (1, 33, 272, 1, 0, 64),    # one full 32-key tile + 1 key, 272 heads
+    (1, 1, 128, 1, 0, 128),    # one key, 128 heads: 8-wave d = 128 launch
+    (1, 2, 256, 2, 1, 128),
+])
+def test_tiny_sequences_with_many_heads(B, S, H, P, rank, d):
+    # Enough heads for the 8-wave launches even though S is tiny: almost every
+    # row of a work unit lies past S, and the one K/V tile is mostly clamped.
+    Q, K, V = _case(B, S, H, P, rank, d, 14)
+    scale = 1.0 / math.sqrt(d)
+    dest = _fused(Q, K, V, rank, P, H)
+    check_dest_layout(dest, B, S, H, d, P, rank)
+    rows = sampled_rows(Workload("t", B, S, H, P, rank, d, 14))
+    _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, "tiny S %r" % ((B, S, H, P, rank, d),))
+    Xq, Xk, Xv = make_qkv(B, S, H, d, 15)
+    io = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused_io(_dev4(Xq), _dev4(Xk), _dev4(Xv), rank, P, io)
+    _sync()
+    G = [oracle.gather(x, H, P, rank) for x in (Xq, Xk, Xv)]
+    np.testing.assert_array_equal(to_host_bits(io), _fused(*G, rank, P, H))
+
+
 @pytest.mark.parametrize("H,d", [(64, 128), (4, 64)])  # P = 2: 8-wave and 4-wave launches
 @pytest.mark.parametrize("pattern", ["rising", "spikes", "offset", "tiny"])
 def test_running_max_rises_and_jumps(H, d, pattern):
