@@ -16,6 +16,7 @@ SHAPES = [
     (2, 200, 8, 8, 3, 128),
     (1, 520, 64, 1, 0, 128),   # 8-wave workgroups
     (3, 129, 9, 3, 2, 64),
+    (2, 1100, 64, 2, 1, 64),   # d = 64, two row blocks per wave on 32-key tiles
 ]
 
 
