@@ -24,7 +24,8 @@
 //  * P^T is fed from those registers (rounded to bf16) as the B operand of
 //    O^T += V^T P^T; V^T comes from the key-major V tile through the gfx950
 //    transposing LDS read ds_read_b64_tr_b16;
-//  * K and V tiles (64 keys; 32 with RB = 2) go global -> LDS with global_load_lds_dwordx4
+//  * K and V tiles (64 keys; 32 with RB = 2) go global -> LDS with
+//    global_load_lds_dwordx4
 //    (no VGPR staging), through a ring of three buffers, one tile ahead;
 //    the operand reads of an iteration's first MFMAs are issued before its
 //    barrier, at the end of the previous iteration;
@@ -74,7 +75,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
-constexpr int kPF = 2;         // operand prefetch distance, in MFMAs
+constexpr int kPF = 2;  // operand prefetch distance, in LDS fragments (each feeds RB MFMAs)
 
 struct AttnArgs {
     const uint16_t *q;
