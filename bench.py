@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seq-len", type=int, default=0, metavar="S",
+                    help="time the workload's heads and head dim at another sequence length "
+                         "(a multiple of its P); the CPU baseline and counter figures then do not apply")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-io", action="store_true",
                     help="skip the timings with the pre-attention exchange (detail.io)")
@@ -283,6 +286,11 @@ def main():
     from ua_inputs import SENTINEL_BITS, WORKLOADS, workload_qkv
 
     w = WORKLOADS[args.workload]
+    if args.seq_len:
+        if args.seq_len % w.P:
+            sys.exit("--seq-len must be a multiple of P = %d" % w.P)
+        w = dataclasses.replace(w, name="%s_S%d" % (w.name, args.seq_len), S=args.seq_len, sampled=True)
+        args.no_cpu = True
     dev = torch.device("cuda:0")
     Q, K, V = workload_qkv(w)
 

@@ -809,18 +809,27 @@ __global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chun
 // Launch shape of the attention kernel for a problem: waves per workgroup,
 // 32-row blocks per wave, keys per K/V tile.  8 waves (one K/V tile per 256
 // query rows) when that still gives at least half a workgroup per CU, else
-// 4.  For d = 64 with at least 128 units of 512 rows, 8 waves of two row
-// blocks each on 32-key tiles (each LDS operand fragment feeds two MFMAs).
+// 4.  For d = 64, 8 waves of two row blocks each on 32-key tiles (512 rows
+// per unit; each LDS operand fragment feeds two MFMAs, ~4% faster per row)
+// when that also gives at least 128 units and its estimated time -- rounds
+// of units over the MI355X's 256 CUs times the rows a unit processes -- is
+// lower.
 struct LaunchShape {
     int nw, rb, kb;
     int rows() const { return 32 * rb * nw; }
 };
 
+constexpr int64_t kCUs = 256;
+
 LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const auto units = [&](int rows) { return B * Hl * ((S + rows - 1) / rows); };
-    if (d == 64 && units(512) >= 128) return {8, 2, 32};
-    return units(256) >= 128 ? LaunchShape{8, 1, 64} : LaunchShape{4, 1, 64};
+    const auto units = [&](int64_t rows) { return B * Hl * ((S + rows - 1) / rows); };
+    // rounds of units over the CUs times the rows a unit processes
+    const auto cost = [&](int64_t rows) { return (units(rows) + kCUs - 1) / kCUs * (S < rows ? S : rows); };
+    if (units(256) < 128) return {4, 1, 64};
+    // per-row time of the two-row-block shape: 24/25 of the one-row-block one
+    if (d == 64 && units(512) >= 128 && cost(512) * 24 <= cost(256) * 25) return {8, 2, 32};
+    return {8, 1, 64};
 }
 
 template <bool TRACE>

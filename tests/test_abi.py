@@ -162,10 +162,11 @@ def test_measurement_entry_points_validate_like_the_fused_call():
 def test_work_units():
     # 256-row units when that gives at least 128 of them, else 128-row units;
     # d = 64 takes 512-row units (two row blocks per wave) when there are at
-    # least 128 of them
+    # least 128 of them and the rounds over 256 CUs do not make it slower
     assert ua.work_units(1, 65536, 40, 128, 8) == 5 * 256
     assert ua.work_units(2, 32768, 24, 64, 4) == 2 * 6 * 64
     assert ua.work_units(2, 1100, 64, 64, 2) == 2 * 32 * 3
+    assert ua.work_units(2, 16384, 24, 64, 4) == 2 * 6 * 64    # 384 units of 512 rows = 1.5 rounds
     assert ua.work_units(1, 4096, 48, 64, 2) == 24 * 8        # 24*8 >= 128 -> 512-row units
     assert ua.work_units(1, 4096, 24, 64, 2) == 12 * 16       # 12*8 < 128 -> 256-row units
     assert ua.work_units(1, 16384, 24, 128, 8) == 3 * 64
