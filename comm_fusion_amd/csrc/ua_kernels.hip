@@ -183,7 +183,7 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
 // at the start, when every wave has its normalised rows ready (a workgroup
 // barrier), when every wave's epilogue stores have completed (vmcnt(0) and a
 // barrier), and the shader-clock cycles from start to end.
-template <int D, int NW, int RB, int KB, bool TRACE>
+template <int D, int NW, int RB, int KB, int KS, bool TRACE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd(AttnArgs a)
 {
@@ -195,30 +195,39 @@ void attn_fwd(AttnArgs a)
     constexpr int KNB = KB / 32;             // 32-key blocks per K/V tile
     constexpr int TILE = KB * D * 2;         // bytes of one K (or V) tile
     constexpr int NCP = TILE / 1024;         // 1 KiB global->LDS copies per tile
-    // With at least as many copies as waves, every wave copies NLD chunks of
-    // K and of V; with fewer, waves [0, NCP) copy K and [NCP, 2 NCP) copy V.
-    constexpr bool SPLIT = NCP < NW;
-    constexpr int NLD = SPLIT ? 1 : NCP / NW;
+    constexpr int NWG = NW / KS;             // waves per key group
+    // With at least as many copies as waves in a key group, every wave copies
+    // NLD chunks of K and of V; with fewer, the group's waves [0, NCP) copy K
+    // and [NCP, 2 NCP) copy V.
+    constexpr bool SPLIT = NCP < NWG;
+    constexpr int NLD = SPLIT ? 1 : NCP / NWG;
     constexpr int CPG = KB / 16;             // 1 KiB copies per 32-column group
     constexpr int KK = D / 16;               // MFMA k-steps over d for S^T
     constexpr int DB = D / 32;               // 32-row blocks of O^T over d
     constexpr int GB = KB * 64;              // bytes of one 32-column group of a tile
     constexpr int RW = 32 * RB;              // query rows per wave
-    constexpr int BR = RW * NW;              // query rows per work unit
-    static_assert(SPLIT ? 2 * NCP <= NW : NCP % NW == 0, "tile split");
+    constexpr int BR = RW * NWG;             // query rows per work unit
+    static_assert(SPLIT ? 2 * NCP <= NWG : NCP % NWG == 0, "tile split");
+    static_assert(NW % KS == 0 && (KS == 1 || (KS == 2 && RB == 1)), "key groups");
     static_assert(KB % 32 == 0 && GB == CPG * 1024, "tile geometry");
-
-    // Three K and three V tile buffers (a ring: tile j lives in buffer j % 3).
-    // Every LDS read in this kernel is an explicit instruction (lds_b128,
-    // lds_tr16) with exact waits, so the compiler needs no alias information
-    // about these arrays.
-    __shared__ __attribute__((aligned(1024))) unsigned char ks[3 * TILE];
-    __shared__ __attribute__((aligned(1024))) unsigned char vs[3 * TILE];
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // KS key groups of NWG waves each: the groups work on the same query
+    // rows, each on its own share of the K/V tiles, and are combined at the
+    // end.  wq is the wave's index within its group.
+    const int grp = KS == 1 ? 0 : wave / NWG;
+    const int wq = wave - grp * NWG;
+
+    // Per key group, three K and three V tile buffers (a ring: tile j lives
+    // in buffer j % 3).  Every LDS read in the main loop is an explicit
+    // instruction (lds_b128, lds_tr16) with exact waits, so the compiler
+    // needs no alias information about these buffers.
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[2 * KS * 3 * TILE];
+    lds_u8 *const ks = (lds_u8 *)lds_all + grp * 3 * TILE;
+    lds_u8 *const vs = (lds_u8 *)lds_all + (KS + grp) * 3 * TILE;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
     const int il = lane & 31;  // query row of this lane within each row block
     const int g = lane >> 5;   // half-wave
     const int i16 = lane & 15;
@@ -236,9 +245,16 @@ void attn_fwd(AttnArgs a)
     // [p*S/P, (p+1)*S/P) back to back), read in place.
     const int rs = a.in_heads * D;  // elements between sequence rows
     const int64_t head = (b * S * a.in_heads + a.in_head0 + h) * D;
+    // Keys of this wave's group: the KS groups split the K/V tiles evenly
+    // (KS = 2 is only launched for an even tile count, so every group runs
+    // the same iterations and barriers, and every group has a full first
+    // tile).  Skv keys starting at key kvbase.
+    const int ntiles = (int)((S + KB - 1) / KB) / KS;
+    const int64_t kvbase = (int64_t)grp * ntiles * KB;
+    const int64_t Skv = S - kvbase < (int64_t)ntiles * KB ? S - kvbase : (int64_t)ntiles * KB;
     const uint16_t *qh = a.q + head;
-    const uint16_t *kh = a.k + head;
-    const uint16_t *vh = a.v + head;
+    const uint16_t *kh = a.k + head + kvbase * rs;
+    const uint16_t *vh = a.v + head + kvbase * rs;
 
     // LDS tile layouts (filled by whole-wave 1 KiB global->LDS copies, lane
     // L of a copy landing at byte 16*L, so a layout is just a per-lane choice
@@ -258,15 +274,15 @@ void attn_fwd(AttnArgs a)
     const unsigned k_chunk = (unsigned)((lane & 3) ^ ((lane >> 4) & 3)) * 16;  // bytes
     const unsigned v_chunk = (unsigned)(lane & 3) * 16;
     // First copy of this wave in a tile (wave-uniform), and whether it copies.
-    const int kcp0 = SPLIT ? wave : wave * NLD;
-    const int vcp0 = SPLIT ? wave - NCP : wave * NLD;
-    const bool kcopies = !SPLIT || wave < NCP;
-    const bool vcopies = !SPLIT || (wave >= NCP && wave < 2 * NCP);
+    const int kcp0 = SPLIT ? wq : wq * NLD;
+    const int vcp0 = SPLIT ? wq - NCP : wq * NLD;
+    const bool kcopies = !SPLIT || wq < NCP;
+    const bool vcopies = !SPLIT || (wq >= NCP && wq < 2 * NCP);
     // Source address = wave-uniform base (scalar registers) + a non-negative
     // 32-bit per-lane byte offset.  Rows past S (last, partial tile) are
     // clamped to row S-1: finite data that the softmax masks out.
     // (S < 2^31 rows, so tile arithmetic fits 32-bit scalar registers.)
-    const int S32 = (int)S;
+    const int S32 = (int)Skv;
     // per-lane byte offsets of a full tile (the same for every tile)
     unsigned koff[NLD], voff[NLD];
 #pragma unroll
@@ -313,7 +329,7 @@ void attn_fwd(AttnArgs a)
     u32x4 qf[RB][KK];  // B operand of S^T = K Q^T: lane holds Q[s][16kk + 8g .. +7]
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        s_q[rb] = (int64_t)qt * BR + wave * RW + rb * 32 + il;
+        s_q[rb] = (int64_t)qt * BR + wq * RW + rb * 32 + il;
         const int64_t s_ld = s_q[rb] < S ? s_q[rb] : S - 1;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
@@ -477,8 +493,7 @@ void attn_fwd(AttnArgs a)
     // run ahead through three-buffer rings (iteration t copies K_{t+3} and
     // V_{t+1}), so the operand reads of the next iteration's first MFMAs can
     // be issued before its barrier.
-    const int ntiles = (int)((S + KB - 1) / KB);
-    const int valid_last = (int)(S - (int64_t)(ntiles - 1) * KB);
+    const int valid_last = (int)(Skv - (int64_t)(ntiles - 1) * KB);
     f32x16 s_cur[RB][KNB], s_nxt[RB][KNB];         // S_t, S_{t+1}
     u32x4 p_cur[RB][2 * KNB], p_prv[RB][2 * KNB];  // packed P_t, P_{t-1}
     auto rotate = [&]() {
@@ -682,6 +697,46 @@ void attn_fwd(AttnArgs a)
         pv(t % 3, p_cur);
     }
 
+    // ---- key groups: group 1 hands its partial O, m and l to the group-0 wave
+    // with the same rows (same lane layout) through LDS, free after the loop;
+    // that wave merges them, O = O0 a0 + O1 a1 and l = l0 a0 + l1 a1 with
+    // a_i = 2^(m_i - max(m0, m1)), and alone stores the rows.
+    if constexpr (KS == 2) {
+        constexpr int NX = RB * DB * 16 + 2 * RB;  // floats per lane
+        static_assert(NWG * NX * 64 * 4 <= 2 * KS * 3 * TILE, "combine area");
+        typedef __attribute__((address_space(3))) float lds_f32;
+        lds_f32 *const xb = (lds_f32 *)lds_all + wq * NX * 64 + lane;
+        sync_all();
+        if (grp == 1) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) xb[((rb * DB + db) * 16 + r) * 64] = oacc[rb][db][r];
+                xb[(RB * DB * 16 + rb) * 64] = m_run[rb];
+                xb[(RB * DB * 16 + RB + rb) * 64] = l_run[rb];
+            }
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float m1 = xb[(RB * DB * 16 + rb) * 64];
+                const float l1 = xb[(RB * DB * 16 + RB + rb) * 64];
+                const float m = fmaxf(m_run[rb], m1);
+                const float a0 = __builtin_amdgcn_exp2f(m_run[rb] - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        oacc[rb][db][r] = oacc[rb][db][r] * a0 + xb[((rb * DB + db) * 16 + r) * 64] * a1;
+                l_run[rb] = l_run[rb] * a0 + l1 * a1;
+                m_run[rb] = m;
+            }
+        }
+    }
+
     // ---- epilogue: normalise and store this lane's half of each of its
     // rows straight into the destination slot (region p, row i, head g0 + h).
     float inv[RB];
@@ -695,7 +750,7 @@ void attn_fwd(AttnArgs a)
     const Placement &o = a.out;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        if (s_q[rb] < S) {
+        if (s_q[rb] < S && grp == 0) {
             const int64_t p = s_q[rb] / o.region_rows;
             const int64_t i = s_q[rb] - p * o.region_rows;
             uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + o.head0 + h) * D;
@@ -728,11 +783,11 @@ void attn_fwd(AttnArgs a)
 
 // Epilogue stores alone: the attention kernel's grid, work-unit order and
 // per-lane store pattern (8-byte chunks of one row per lane, placed by the
-// same Placement arithmetic, RB row blocks per wave), with a closed-form
-// value instead of attention output: element (s, head g, column c) gets bf16
-// bits (7s + 13g + 3c) & 0x3FFF (finite, positive).  Measures what the
-// destination layout sustains.
-template <int D, int NW, int RB>
+// same Placement arithmetic, RB row blocks per wave, only key group 0
+// storing), with a closed-form value instead of attention output: element
+// (s, head g, column c) gets bf16 bits (7s + 13g + 3c) & 0x3FFF (finite,
+// positive).  Measures what the destination layout sustains.
+template <int D, int NW, int RB, int KS>
 __global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S, int32_t Hl, int32_t n_qtiles,
                                                          int32_t n_units)
 {
@@ -744,9 +799,10 @@ __global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S,
     const int bh = unit / n_qtiles;
     const int h = bh % Hl;
     const int64_t b = bh / Hl;
+    if (wave >= NW / KS) return;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int64_t s_q = (int64_t)qt * (32 * RB * NW) + wave * (32 * RB) + rb * 32 + il;
+        const int64_t s_q = (int64_t)qt * (32 * RB * NW / KS) + wave * (32 * RB) + rb * 32 + il;
         if (s_q >= S) continue;
         const int64_t p = s_q / o.region_rows;
         const int64_t i = s_q - p * o.region_rows;
@@ -815,8 +871,8 @@ __global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chun
 // of units over the MI355X's 256 CUs times the rows a unit processes -- is
 // lower.
 struct LaunchShape {
-    int nw, rb, kb;
-    int rows() const { return 32 * rb * nw; }
+    int nw, rb, kb, ks;
+    int rows() const { return 32 * rb * nw / ks; }
 };
 
 constexpr int64_t kCUs = 256;
@@ -826,19 +882,28 @@ LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
     const auto units = [&](int64_t rows) { return B * Hl * ((S + rows - 1) / rows); };
     // rounds of units over the CUs times the rows a unit processes
     const auto cost = [&](int64_t rows) { return (units(rows) + kCUs - 1) / kCUs * (S < rows ? S : rows); };
-    if (units(256) < 128) return {4, 1, 64};
+    if (units(256) < 128) {
+        // 128-row units: two key groups of 4 waves on 32-key tiles (two waves
+        // per SIMD) when the tile count is even, else 4 waves (one per SIMD)
+        const int64_t nt = (S + 31) / 32;
+        if (nt >= 2 && nt % 2 == 0) return {8, 1, 32, 2};
+        return {4, 1, 64, 1};
+    }
     // per-row time of the two-row-block shape: 24/25 of the one-row-block one
-    if (d == 64 && units(512) >= 128 && cost(512) * 24 <= cost(256) * 25) return {8, 2, 32};
-    return {8, 1, 64};
+    if (d == 64 && units(512) >= 128 && cost(512) * 24 <= cost(256) * 25) return {8, 2, 32, 1};
+    return {8, 1, 64, 1};
 }
 
 template <bool TRACE>
 const void *attention_kernel(int d, const LaunchShape &ls)
 {
-    if (d == 128)
-        return ls.nw == 8 ? (const void *)attn_fwd<128, 8, 1, 64, TRACE> : (const void *)attn_fwd<128, 4, 1, 64, TRACE>;
-    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, TRACE>;
-    return ls.nw == 8 ? (const void *)attn_fwd<64, 8, 1, 64, TRACE> : (const void *)attn_fwd<64, 4, 1, 64, TRACE>;
+    if (d == 128) {
+        if (ls.ks == 2) return (const void *)attn_fwd<128, 8, 1, 32, 2, TRACE>;
+        return ls.nw == 8 ? (const void *)attn_fwd<128, 8, 1, 64, 1, TRACE> : (const void *)attn_fwd<128, 4, 1, 64, 1, TRACE>;
+    }
+    if (ls.ks == 2) return (const void *)attn_fwd<64, 8, 1, 32, 2, TRACE>;
+    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, 1, TRACE>;
+    return ls.nw == 8 ? (const void *)attn_fwd<64, 8, 1, 64, 1, TRACE> : (const void *)attn_fwd<64, 4, 1, 64, 1, TRACE>;
 }
 
 }  // namespace
@@ -884,12 +949,14 @@ hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const P
     int32_t n_units = (int32_t)attention_units(B, S, Hl, d);
     void *args[] = {&o, &S64, &Hl32, &n_qtiles, &n_units};
     const void *fn;
-    if (d == 128)
-        fn = ls.nw == 8 ? (const void *)epilogue_only<128, 8, 1> : (const void *)epilogue_only<128, 4, 1>;
+    if (ls.ks == 2)
+        fn = d == 128 ? (const void *)epilogue_only<128, 8, 1, 2> : (const void *)epilogue_only<64, 8, 1, 2>;
+    else if (d == 128)
+        fn = ls.nw == 8 ? (const void *)epilogue_only<128, 8, 1, 1> : (const void *)epilogue_only<128, 4, 1, 1>;
     else if (ls.rb == 2)
-        fn = (const void *)epilogue_only<64, 8, 2>;
+        fn = (const void *)epilogue_only<64, 8, 2, 1>;
     else
-        fn = ls.nw == 8 ? (const void *)epilogue_only<64, 8, 1> : (const void *)epilogue_only<64, 4, 1>;
+        fn = ls.nw == 8 ? (const void *)epilogue_only<64, 8, 1, 1> : (const void *)epilogue_only<64, 4, 1, 1>;
     return hipLaunchKernel(fn, dim3(n_units), dim3(64 * ls.nw), args, 0, stream);
 }
 
