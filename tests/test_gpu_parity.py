@@ -79,6 +79,9 @@ SMALL = [
     # d = 64 with enough units of 512 rows for two row blocks per wave on
     # 32-key tiles: 1100 = 34 tiles + 12 keys, 2 units of 512 rows + 76
     (2, 1100, 64, 2, 1, 64, 13),
+    # few units: two key groups of 4 waves on 32-key tiles; 1000 = 32 tiles
+    # (16 per group), the last one 8 keys; units of 128 rows with a ragged last
+    (2, 1000, 4, 2, 1, 128, 16),
 ]
 
 
