@@ -10,11 +10,14 @@
 // output-tile owner issues the exchange stores itself, then moves on).
 //
 // Design for CDNA4, not a translation of the pages' FlashAttention-3/4:
-//  * a workgroup of NW wave64s (8, or 4 for small problems) owns 32*RB*NW
+//  * a workgroup of NW wave64s (8, or 4 for small problems) owns 32*RB*NW/KS
 //    query rows of one (batch, local head); each wave owns RB blocks of 32
 //    rows (RB = 2 for d = 64, where the registers allow it: each K or V
-//    fragment read from LDS then feeds two MFMAs).  All waves share each
-//    K/V tile, so a tile crosses L2 -> LDS once per 32*RB*NW rows;
+//    fragment read from LDS then feeds two MFMAs).  With KS = 2 (launches
+//    with fewer units than CUs) two key groups of waves share the rows, each
+//    taking half the K/V tiles, and merge their partial results through LDS
+//    at the end.  The waves of a key group share each K/V tile, so a tile
+//    crosses L2 -> LDS once per 32*RB*NW/KS rows;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K streams from LDS as the A operand and the
 //    wave's Q rows stay in VGPRs as the B operand.  The accumulator layout
