@@ -46,11 +46,43 @@ def sweep_shapes(n=32, seed=2026):
 SHAPES = sweep_shapes()
 
 
+def sweep_shapes_b(n=16, seed=2027):
+    """Shapes aimed at the two launch shapes with extra structure: even draws
+    are d = 64 with enough 512-row units for two row blocks per wave (units
+    halve against 256-row ones: B*Hl*ceil(S/512) >= 128 and fewer rounds over
+    256 CUs), odd draws have fewer than 128 units of 256 rows and an even
+    32-key tile count (two key groups per workgroup)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        P = int(rng.choice([1, 2, 3, 4]))
+        B = int(rng.integers(1, 3))
+        if len(out) % 2 == 0:
+            d, Hl = 64, int(rng.choice([40, 64, 96]))
+            S = P * int(rng.integers(700 // P, 1 + 1400 // P))
+            u512, u256 = B * Hl * -(-S // 512), B * Hl * -(-S // 256)
+            if u512 < 128 or -(-u512 // 256) * 2 > -(-u256 // 256):
+                continue
+        else:
+            d, Hl = int(rng.choice([64, 128])), int(rng.choice([1, 2, 3]))
+            S = P * int(rng.integers(1, 1 + 1500 // P))
+            nt = -(-S // 32)
+            if B * Hl * -(-S // 256) >= 128 or nt < 2 or nt % 2:
+                continue
+        if B * S * Hl * P * d > 2.5e7:
+            continue
+        out.append((B, S, Hl * P, P, int(rng.integers(0, P)), d, 300 + len(out)))
+    return out
+
+
+SHAPES_B = sweep_shapes_b()
+
+
 def _dev(a):
     return to_dev(a).view(*a.shape)
 
 
-@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SHAPES)
+@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SHAPES + SHAPES_B)
 def test_sweep(B, S, H, P, rank, d, seed):
     import torch
     Hl = H // P
