@@ -220,9 +220,12 @@ def test_tiny_sequences_with_many_heads(B, S, H, P, rank, d):
     np.testing.assert_array_equal(to_host_bits(io), _fused(*G, rank, P, H))
 
 
-@pytest.mark.parametrize("H,d", [(64, 128), (4, 64)])  # P = 2: 8-wave and 4-wave launches
+# P = 2.  S = 1030 (33 tiles of 32 keys): 8-wave launch (64 heads) and 4-wave
+# launch (4 heads); S = 1024 (32 tiles): two key groups, whose partial results
+# with very different maxima are merged at the end.
+@pytest.mark.parametrize("H,d,S", [(64, 128, 1030), (4, 64, 1030), (4, 128, 1024), (4, 64, 1024)])
 @pytest.mark.parametrize("pattern", ["rising", "spikes", "offset", "tiny"])
-def test_running_max_rises_and_jumps(H, d, pattern):
+def test_running_max_rises_and_jumps(H, d, S, pattern):
     # Scores whose running max keeps rising along the keys (K rows scaled by
     # 0.25 .. 3.25), or jumps far past it in the middle of the sequence (three
     # keys scaled by 60: against the earlier max, exp of such a score
@@ -232,7 +235,7 @@ def test_running_max_rises_and_jumps(H, d, pattern):
     # few hundred away from zero, far outside exp's fp32 range), and keys
     # scaled down to ~1e-3 (nearly uniform weights).
     from ua_inputs import to_bf16_bits
-    B, S, P, rank = 1, 1030, 2, 1
+    B, P, rank = 1, 2, 1
     Q, K, V = _case(B, S, H, P, rank, d, 12)
     Kf = bits_to_f64(K)
     if pattern == "rising":
