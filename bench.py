@@ -1,6 +1,7 @@
 """Benchmark: fused Ulysses-shard attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--seq-len S]
+                    [--no-cpu] [--no-io] [--rounds R] [--cpu-all]
 
 One step = one attn_ulysses_fused call over the whole workload (attention over
 the rank's Hl heads, each output tile stored into its post-All-to-All slot).
