@@ -14,7 +14,7 @@
 //    query rows of one (batch, local head); each wave owns RB blocks of 32
 //    rows (RB = 2 for d = 64, where the registers allow it: each K or V
 //    fragment read from LDS then feeds two MFMAs).  With KS = 2 (launches
-//    with fewer units than CUs) two key groups of waves share the rows, each
+//    with fewer than 128 units of 256 rows) two key groups of waves share the rows, each
 //    taking half the K/V tiles, and merge their partial results through LDS
 //    at the end.  The waves of a key group share each K/V tile, so a tile
 //    crosses L2 -> LDS once per 32*RB*NW/KS rows;
@@ -27,9 +27,9 @@
 //  * P^T is fed from those registers (rounded to bf16) as the B operand of
 //    O^T += V^T P^T; V^T comes from the key-major V tile through the gfx950
 //    transposing LDS read ds_read_b64_tr_b16;
-//  * K and V tiles (64 keys; 32 with RB = 2) go global -> LDS with
-//    global_load_lds_dwordx4
-//    (no VGPR staging), through a ring of three buffers, one tile ahead;
+//  * K and V tiles (64 keys; 32 with RB = 2 or KS = 2) go global -> LDS
+//    with global_load_lds_dwordx4 (no VGPR staging), through rings of three
+//    buffers, each copy issued two iterations before its tile is used;
 //    the operand reads of an iteration's first MFMAs are issued before its
 //    barrier, at the end of the previous iteration;
 //  * software pipeline: in steady state, iteration t interleaves the
@@ -175,10 +175,11 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
 }
 
 // Template parameters: D head dim; NW waves per workgroup; RB 32-row query
-// blocks per wave; KB keys per K/V tile.  NW = 8: two waves per SIMD, one
-// workgroup per CU.  NW = 4 only runs for shapes with fewer work units than
-// CUs, so it is built for one wave per SIMD (and gets that SIMD's whole
-// register file).  RB = 2 (d = 64 only, where the registers allow it): each
+// blocks per wave; KB keys per K/V tile; KS key groups per workgroup.
+// NW = 8: two waves per SIMD, one workgroup per CU.  NW = 4 only runs for
+// small shapes (fewer than 128 units of 256 rows) whose 32-key tile count
+// cannot be split evenly between two key groups, so it is built for one wave
+// per SIMD (and gets that SIMD's whole register file).  RB = 2 (d = 64 only, where the registers allow it): each
 // K or V fragment read from LDS feeds two MFMAs, one per row block, which
 // halves the LDS operand bytes per flop.
 // TRACE: measurement build with the same arithmetic and output, which also
@@ -866,13 +867,15 @@ __global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chun
 }
 
 // Launch shape of the attention kernel for a problem: waves per workgroup,
-// 32-row blocks per wave, keys per K/V tile.  8 waves (one K/V tile per 256
-// query rows) when that still gives at least half a workgroup per CU, else
-// 4.  For d = 64, 8 waves of two row blocks each on 32-key tiles (512 rows
-// per unit; each LDS operand fragment feeds two MFMAs, ~4% faster per row)
-// when that also gives at least 128 units and its estimated time -- rounds
-// of units over the MI355X's 256 CUs times the rows a unit processes -- is
-// lower.
+// 32-row blocks per wave, keys per K/V tile, key groups.  With at least 128
+// units of 256 rows (half a workgroup per CU): 8 waves on 64-key tiles (one
+// K/V tile per 256 query rows); for d = 64, 8 waves of two row blocks each
+// on 32-key tiles (512 rows per unit; each LDS operand fragment feeds two
+// MFMAs, ~4% faster per row) when that also gives at least 128 units and its
+// estimated time -- rounds of units over the MI355X's 256 CUs times the rows
+// a unit processes -- is at most 25/24 of the other's.  Below 128 units:
+// 128-row units, as two key groups of 4 waves on 32-key tiles when the
+// 32-key tile count is even, else as 4 waves on 64-key tiles.
 struct LaunchShape {
     int nw, rb, kb, ks;
     int rows() const { return 32 * rb * nw / ks; }
