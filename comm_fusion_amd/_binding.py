@@ -104,10 +104,19 @@ def _check_bf16(name, t, numel=None):
         raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
 
 
-def _stream(stream) -> int:
+def _stream(stream, *tensors) -> int:
+    """The stream handle for a call on ``tensors``: they must share one device,
+    and a torch stream passed in must belong to it; None means that device's
+    current stream.  A raw handle (int) is taken as given."""
     import torch
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError("all tensors of a call must be on one device, got %s" % sorted(map(str, devs)))
+    dev = devs.pop() if devs else None
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif dev is not None and hasattr(stream, "device") and torch.device(stream.device) != dev:
+        raise ValueError("stream is on %s but the tensors are on %s" % (stream.device, dev))
     return int(getattr(stream, "cuda_stream", stream))
 
 
@@ -126,7 +135,7 @@ def attn_ulysses_fused(Q, K, V, rank, P, out, scale=None, stream=None):
     _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
     scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
     st = lib().attn_ulysses_fused(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
-                                  ctypes.byref(shp), scale, _stream(stream))
+                                  ctypes.byref(shp), scale, _stream(stream, Q, K, V, out))
     if st != UA_OK:
         raise UAError("attn_ulysses_fused", st)
 
@@ -139,7 +148,7 @@ def attn_serial(Q, K, V, rank, P, O_local, scale=None, stream=None):
     _check_bf16("O_local", O_local, Q.numel())
     scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
     st = lib().attn_serial(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(O_local),
-                           ctypes.byref(shp), scale, _stream(stream))
+                           ctypes.byref(shp), scale, _stream(stream, Q, K, V, O_local))
     if st != UA_OK:
         raise UAError("attn_serial", st)
 
@@ -153,7 +162,7 @@ def a2a_permute(O_local, rank, P, out, stream=None):
     _check_bf16("O_local", O_local)
     _check_bf16("out", out, B * S * Hl * int(P) * d)
     st = lib().a2a_permute(_ptr(O_local), int(rank), int(P), _ptr(out), ctypes.byref(shp),
-                           _stream(stream))
+                           _stream(stream, O_local, out))
     if st != UA_OK:
         raise UAError("a2a_permute", st)
 
@@ -182,7 +191,7 @@ def attn_ulysses_fused_io(Xq, Xk, Xv, rank, P, out, scale=None, stream=None):
     _check_bf16("out", out, n)
     scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
     st = lib().attn_ulysses_fused_io(_ptr(Xq), _ptr(Xk), _ptr(Xv), int(rank), int(P), _ptr(out),
-                                     ctypes.byref(shp), scale, _stream(stream))
+                                     ctypes.byref(shp), scale, _stream(stream, Xq, Xk, Xv, out))
     if st != UA_OK:
         raise UAError("attn_ulysses_fused_io", st)
 
@@ -193,7 +202,7 @@ def a2a_gather(X, rank, P, X_local, stream=None):
     shp = _seq_shape(X, P)
     _check_bf16("X", X, shp.B * shp.S * shp.H * shp.d)
     _check_bf16("X_local", X_local, shp.B * shp.S * (shp.H // int(P)) * shp.d)
-    st = lib().a2a_gather(_ptr(X), int(rank), int(P), _ptr(X_local), ctypes.byref(shp), _stream(stream))
+    st = lib().a2a_gather(_ptr(X), int(rank), int(P), _ptr(X_local), ctypes.byref(shp), _stream(stream, X, X_local))
     if st != UA_OK:
         raise UAError("a2a_gather", st)
 
@@ -216,7 +225,7 @@ def attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=No
         raise TypeError("trace must be a contiguous int64 GPU tensor of %d elements" % (4 * n_units))
     scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
     st = lib().attn_ulysses_fused_trace(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
-                                        ctypes.byref(shp), scale, _stream(stream), _ptr(trace))
+                                        ctypes.byref(shp), scale, _stream(stream, Q, K, V, out, trace), _ptr(trace))
     if st != UA_OK:
         raise UAError("attn_ulysses_fused_trace", st)
 
@@ -225,6 +234,6 @@ def epilogue_store_only(B, S, H, d, rank, P, out, stream=None):
     """The fused call's epilogue stores alone (closed-form values) into ``out``."""
     shp = Shape(int(B), int(S), int(H), int(d))
     _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
-    st = lib().ua_epilogue_store_only(int(rank), int(P), _ptr(out), ctypes.byref(shp), _stream(stream))
+    st = lib().ua_epilogue_store_only(int(rank), int(P), _ptr(out), ctypes.byref(shp), _stream(stream, out))
     if st != UA_OK:
         raise UAError("ua_epilogue_store_only", st)

@@ -55,3 +55,18 @@ def test_device_tensor_sizes_and_layouts_are_checked():
     with pytest.raises(ua.UAError) as e:    # rank out of range reaches the C validation
         ua.attn_ulysses_fused(q, q, q, 2, 2, out)
     assert e.value.status == ua.UA_ERR_RANK
+
+
+def test_tensors_of_one_call_must_share_a_device():
+    # the device check runs before any stream or device is touched
+    from types import SimpleNamespace
+    from comm_fusion_amd import _binding
+    a = SimpleNamespace(device=torch.device("cuda", 0))
+    b = SimpleNamespace(device=torch.device("cuda", 1))
+    with pytest.raises(ValueError):
+        _binding._stream(None, a, b)
+    s = SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=1234)
+    with pytest.raises(ValueError):
+        _binding._stream(s, a, a)
+    assert _binding._stream(s, b, b) == 1234
+    assert _binding._stream(5678, a, a) == 5678      # a raw handle is taken as given
