@@ -35,8 +35,9 @@
  * Output buffers must not overlap the inputs.
  *
  * Pointers Q, K, V, out, O_local are DEVICE pointers on the current HIP
- * device, 16-byte aligned.  `stream` is a hipStream_t (NULL = default
- * stream).  Calls are asynchronous: they return after the launch.
+ * device, 16-byte aligned.  `stream` is a hipStream_t of that device
+ * (NULL = its default stream).  Calls are asynchronous: they return after
+ * the launch.
  *
  * Errors: every call returns a status code and never prints or aborts.
  * Arguments are validated on the host before any device access, in this
