@@ -255,6 +255,29 @@ def test_running_max_rises_and_jumps(H, d, S, pattern):
     _compare_rows(dest, Q, K, V, rows, H, P, rank, scale, pattern)
 
 
+@pytest.mark.parametrize("B,S,H,P,rank,d", [
+    (1, 524290, 2, 2, 1, 64),    # 2^19 + 2 keys: 16385 tiles of 32 keys, the last holding 2
+    (1, 262150, 2, 2, 0, 128),   # 2^18 + 6 keys: 4097 tiles of 64 keys, the last holding 6
+])
+def test_very_long_sequences(B, S, H, P, rank, d):
+    # Sequences well past the benchmarked ones, with one local head: tile and
+    # row indices far beyond the workloads', ragged last Q and KV tiles.
+    # Sampled rows against the oracle, the full-buffer layout, and the
+    # fused-io call bit-equal to gather + fused.
+    seed = 16
+    Q, K, V = _case(B, S, H, P, rank, d, seed)
+    dest = _fused(Q, K, V, rank, P, H)
+    check_dest_layout(dest, B, S, H, d, P, rank)
+    rows = sampled_rows(Workload("t", B, S, H, P, rank, d, seed, sampled=True), n_per_head=16)
+    _compare_rows(dest, Q, K, V, rows, H, P, rank, 1.0 / math.sqrt(d), "S = %d" % S)
+    Xq, Xk, Xv = make_qkv(B, S, H, d, seed + 1)
+    io = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused_io(_dev4(Xq), _dev4(Xk), _dev4(Xv), rank, P, io)
+    _sync()
+    G = [oracle.gather(x, H, P, rank) for x in (Xq, Xk, Xv)]
+    np.testing.assert_array_equal(to_host_bits(io), _fused(*G, rank, P, H))
+
+
 @pytest.mark.parametrize("name", ["dit_image", "dit_long", "video_dit", "mixed"])
 def test_workloads_at_full_size(name):
     # The configurations the benchmark times, at full size: sampled rows
