@@ -1,10 +1,15 @@
 """Benchmark: fused Ulysses-shard attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--seq-len S]
-                    [--no-cpu] [--no-io] [--rounds R] [--cpu-all]
+                    [--no-cpu] [--no-split] [--no-io] [--cpu-seconds T] [--rounds R]
+                    [--cpu-all] [--full-limit T] [--calibrate-copy MIB]
 
 One step = one attn_ulysses_fused call over the whole workload (attention over
 the rank's Hl heads, each output tile stored into its post-All-to-All slot).
+Workloads with fewer query tiles than CUs (ua.key_split > 1) run the calls
+with a workspace instead (attn_ulysses_fused_ws / attn_serial_ws: each query
+tile's keys split over several workgroups); detail.unsplit then times the
+plain call beside them, and --no-split times the plain calls throughout.
 Inputs are seeded synthetic bf16 tensors already resident in HBM when timing
 starts.  Prints ONE JSON line:
   value     attention TFLOP/s of the fused call, counting 4*S^2*d per
@@ -56,6 +61,8 @@ def parse():
                     help="time the workload's heads and head dim at another sequence length "
                          "(a multiple of its P); the CPU baseline and counter figures then do not apply")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-split", action="store_true",
+                    help="time the calls without a workspace even where a key split would run")
     ap.add_argument("--no-io", action="store_true",
                     help="skip the timings with the pre-attention exchange (detail.io)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -304,8 +311,15 @@ def main():
     o_local = torch.empty_like(q)
     torch.cuda.synchronize()
 
-    fused = lambda: ua.attn_ulysses_fused(q, k, v, w.rank, w.P, dest)  # noqa: E731
-    alone = lambda: ua.attn_serial(q, k, v, w.rank, w.P, o_local)       # noqa: E731
+    n_split = 1 if args.no_split else ua.key_split(w.B, w.S, w.H, w.d, w.P)
+    plain = lambda: ua.attn_ulysses_fused(q, k, v, w.rank, w.P, dest)  # noqa: E731
+    if n_split > 1:
+        ws = ua.new_workspace(w.B, w.S, w.H, w.d, w.P, dev)
+        fused = lambda: ua.attn_ulysses_fused_ws(q, k, v, w.rank, w.P, dest, ws)  # noqa: E731
+        alone = lambda: ua.attn_serial_ws(q, k, v, w.rank, w.P, o_local, ws)      # noqa: E731
+    else:
+        fused = plain
+        alone = lambda: ua.attn_serial(q, k, v, w.rank, w.P, o_local)  # noqa: E731
     perm = lambda: ua.a2a_permute(o_local, w.rank, w.P, dest)           # noqa: E731
     scratch_dest = torch.empty_like(dest)
     store_only = lambda: ua.epilogue_store_only(w.B, w.S, w.H, w.d, w.rank, w.P, scratch_dest)  # noqa: E731
@@ -315,6 +329,8 @@ def main():
         perm()
 
     fns = {"fused": fused, "serial": serial, "alone": alone, "perm": perm, "store_only": store_only}
+    if n_split > 1:
+        fns["unsplit"] = plain
     if not args.no_io:
         # Sequence-partitioned inputs [B][P][S/P][H][d] holding the rank's
         # Q, K, V in its head slots (the other heads are never read).
@@ -358,7 +374,15 @@ def main():
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     med = lambda x: float(np.median(x))  # noqa: E731
     t_f, t_s, t_a, t_p = med(cmp["fused"]), med(per_serial), med(per_alone), med(per_perm)
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name) if n_split == 1 else None
+    unsplit = None
+    if n_split > 1:
+        t_u = med(cmp["unsplit"])
+        unsplit = {"key_split": n_split, "workspace_bytes": ua.workspace_bytes(w.B, w.S, w.H, w.d, w.P),
+                   "unsplit_fused_ms_median": round(t_u, 4),
+                   "unsplit_TFLOPs": round(w.flops / (t_u * 1e-3) / 1e12, 2),
+                   "speedup_split_over_unsplit": round(t_u / t_f, 4),
+                   "note": "the traced call (sclk, epilogue spans) is the unsplit kernel"}
     io = None
     if not args.no_io:
         t_fio, t_sio, t_g = med(cmp["fused_io"]), med(cmp["serial_io"]), med(cmp["gather"])
@@ -384,7 +408,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "P": w.P, "rank": w.rank,
-                   "d": w.d, "Hl": w.Hl, "flops_per_step": w.flops, "causal": False},
+                   "d": w.d, "Hl": w.Hl, "flops_per_step": w.flops, "causal": False,
+                   "key_split": n_split},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
@@ -405,7 +430,8 @@ def main():
             **tr,
             # the same against the peak scaled to the clock the traced call ran at
             "pct_bf16_peak_at_traced_clock": round(100.0 * value / (PEAK_BF16_TFLOPS * tr["sclk_mhz_trace"] / 2400.0), 2)
-            if tr.get("sclk_mhz_trace") else None,
+            if tr.get("sclk_mhz_trace") and n_split == 1 else None,
+            "split": unsplit,
             "io": io,
             "wall_ms_timed_region": round(wall_ms, 3),
             "kernel_code_sha256_16": source_digest(),

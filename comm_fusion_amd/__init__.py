@@ -13,6 +13,10 @@ Names and arguments follow the C calls:
   a2a_permute(O_local, rank, P, out, stream=None)
   attn_ulysses_fused_io(Xq, Xk, Xv, rank, P, out, scale=None, stream=None)
   a2a_gather(X, rank, P, X_local, stream=None)
+  attn_ulysses_fused_ws(Q, K, V, rank, P, out, workspace, scale=None, stream=None)
+  attn_serial_ws(Q, K, V, rank, P, O_local, workspace, scale=None, stream=None)
+  workspace_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
+  new_workspace(B, S, H, d, P, device)  (a zeroed uint8 tensor, or None)
 and, for measurement only,
   attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None)
   epilogue_store_only(B, S, H, d, rank, P, out, stream=None)
@@ -23,8 +27,8 @@ Tensors are torch tensors on the GPU: Q, K, V, O_local bfloat16
 [B][P][S/P][H][d] (or the same bytes viewed as [B][S][H][d]).
 """
 from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # noqa: F401
-                       UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_OK, UAError, a2a_gather, a2a_permute,
-                       attn_serial, attn_ulysses_fused, attn_ulysses_fused_io,
-                       attn_ulysses_fused_trace, dest_bytes,
-                       epilogue_store_only, lib, lib_path, local_bytes, status_string, version,
-                       work_units)
+                       UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_OK, UAError,
+                       a2a_gather, a2a_permute, attn_serial, attn_serial_ws, attn_ulysses_fused,
+                       attn_ulysses_fused_io, attn_ulysses_fused_trace, attn_ulysses_fused_ws,
+                       dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
+                       new_workspace, status_string, version, work_units, workspace_bytes)

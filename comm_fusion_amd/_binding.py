@@ -15,6 +15,7 @@ UA_ERR_RANK = -3
 UA_ERR_ALIGN = -4
 UA_ERR_UNSUPPORTED = -5
 UA_ERR_HIP = -6
+UA_ERR_WORKSPACE = -7
 
 
 class UAError(RuntimeError):
@@ -43,6 +44,12 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError("libulysses_attn.so is not built (%s); run "
                           "`python -m comm_fusion_amd.build` or __graft_entry__.build()" % _LIB_PATH)
+    # torch carries its own copy of the HIP runtime, which its libraries load
+    # under another file name than ours asks for (same SONAME).  Loaded first,
+    # that copy also satisfies this library's dependency; loaded after it, a
+    # second runtime would come in, and torch's device pointers and streams
+    # would be foreign to the one the library launches on.
+    import torch  # noqa: F401
     L = ctypes.CDLL(_LIB_PATH)
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     sp = ctypes.POINTER(Shape)
@@ -70,6 +77,15 @@ def lib() -> ctypes.CDLL:
     L.attn_ulysses_fused_io.restype = i
     L.a2a_gather.argtypes = [vp, i, i, vp, sp, vp]
     L.a2a_gather.restype = i
+    sz = ctypes.c_size_t
+    L.attn_ulysses_fused_ws.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp, sz, vp]
+    L.attn_ulysses_fused_ws.restype = i
+    L.attn_serial_ws.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp, sz, vp]
+    L.attn_serial_ws.restype = i
+    L.ua_workspace_bytes.argtypes = [sp, i]
+    L.ua_workspace_bytes.restype = sz
+    L.ua_key_split.argtypes = [sp, i]
+    L.ua_key_split.restype = i
     _lib = L
     return L
 
@@ -237,3 +253,59 @@ def epilogue_store_only(B, S, H, d, rank, P, out, stream=None):
     st = lib().ua_epilogue_store_only(int(rank), int(P), _ptr(out), ctypes.byref(shp), _stream(stream, out))
     if st != UA_OK:
         raise UAError("ua_epilogue_store_only", st)
+
+
+def workspace_bytes(B, S, H, d, P) -> int:
+    """Workspace bytes the *_ws calls need for this shape (0: no key split)."""
+    return int(lib().ua_workspace_bytes(ctypes.byref(Shape(B, S, H, d)), int(P)))
+
+
+def key_split(B, S, H, d, P) -> int:
+    """Workgroups that share each query tile's keys in a *_ws call (1: none)."""
+    return int(lib().ua_key_split(ctypes.byref(Shape(B, S, H, d)), int(P)))
+
+
+def new_workspace(B, S, H, d, P, device):
+    """A zeroed workspace for the *_ws calls on ``device`` (a uint8 tensor), or
+    None when the shape needs none."""
+    import torch
+    n = workspace_bytes(B, S, H, d, P)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _ws(workspace):
+    """(pointer, bytes) of a workspace tensor, or (0, 0) for None."""
+    if workspace is None:
+        return 0, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous GPU tensor")
+    return int(workspace.data_ptr()), int(workspace.numel() * workspace.element_size())
+
+
+def attn_ulysses_fused_ws(Q, K, V, rank, P, out, workspace, scale=None, stream=None):
+    """attn_ulysses_fused with a workspace (see new_workspace): shapes with fewer
+    query tiles than CUs split each tile's keys over several workgroups."""
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
+    wp, wb = _ws(workspace)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_ulysses_fused_ws(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
+                                     ctypes.byref(shp), scale, wp, wb, _stream(stream, Q, K, V, out, workspace))
+    if st != UA_OK:
+        raise UAError("attn_ulysses_fused_ws", st)
+
+
+def attn_serial_ws(Q, K, V, rank, P, O_local, workspace, scale=None, stream=None):
+    """attn_serial with a workspace (see new_workspace)."""
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("O_local", O_local, Q.numel())
+    wp, wb = _ws(workspace)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_serial_ws(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(O_local),
+                              ctypes.byref(shp), scale, wp, wb, _stream(stream, Q, K, V, O_local, workspace))
+    if st != UA_OK:
+        raise UAError("attn_serial_ws", st)

@@ -2,7 +2,8 @@
 //
 // Host-side only: argument validation (no device access, so it runs on a
 // host without a GPU), placement set-up for the two epilogues, and launches.
-// The library allocates nothing and keeps no state between calls.
+// The library allocates nothing and keeps no state between calls (the *_ws
+// calls use the workspace their caller passes in).
 
 #include "ulysses_attn.h"
 
@@ -13,7 +14,7 @@
 
 namespace {
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;
 
 bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
@@ -90,9 +91,12 @@ ua::Placement local_placement(void *o_local, const ua_shape *shp, int P)
 
 // seq_input: Q, K, V are the sequence-partitioned [B][P][S/P][H][d] inputs
 // of the pre-attention exchange (read in place), else [B][S][Hl][d].
+// want_ws: a *_ws call, whose workspace (ws_bytes bytes) lets the launch
+// split the keys of each query tile over several workgroups.
 int attention_call(const void *Q, const void *K, const void *V, int rank, int P, void *out,
                    const ua_shape *shp, float scale, void *stream, bool fused, uint64_t *trace = nullptr,
-                   bool want_trace = false, bool seq_input = false)
+                   bool want_trace = false, bool seq_input = false, bool want_ws = false,
+                   void *ws = nullptr, size_t ws_bytes = 0)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);
@@ -104,13 +108,20 @@ int attention_call(const void *Q, const void *K, const void *V, int rank, int P,
     if (!Q || !K || !V || !out || (want_trace && !trace)) return UA_ERR_NULL;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || (want_trace && !aligned16(trace)))
         return UA_ERR_ALIGN;
-    const ua::Placement o = fused ? dest_placement(out, shp, rank, P) : local_placement(out, shp, P);
     const int64_t Hl = shp->H / P;
+    const int64_t need = want_ws ? ua::workspace_bytes(shp->B, shp->S, Hl, (int)shp->d) : 0;
+    if (need > 0) {
+        if (!ws) return UA_ERR_NULL;
+        if (!aligned16(ws)) return UA_ERR_ALIGN;
+        if (ws_bytes < (size_t)need) return UA_ERR_WORKSPACE;
+    }
+    const ua::Placement o = fused ? dest_placement(out, shp, rank, P) : local_placement(out, shp, P);
     const int64_t in_heads = seq_input ? shp->H : Hl;
     const int64_t in_head0 = seq_input ? (int64_t)rank * Hl : 0;
     const hipError_t e = ua::launch_attention((const uint16_t *)Q, (const uint16_t *)K,
                                               (const uint16_t *)V, in_heads, in_head0, shp->B, shp->S,
-                                              Hl, (int)shp->d, scale, o, (hipStream_t)stream, trace);
+                                              Hl, (int)shp->d, scale, o, (hipStream_t)stream, trace,
+                                              need > 0 ? ws : nullptr);
     return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
@@ -128,6 +139,38 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P, vo
                 const ua_shape *shp, float scale, void *stream)
 {
     return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false);
+}
+
+int attn_ulysses_fused_ws(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                          const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
+                          void *stream)
+{
+    return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, nullptr, false, false, true,
+                          workspace, workspace_bytes);
+}
+
+int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P, void *O_local,
+                   const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
+                   void *stream)
+{
+    return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false, nullptr, false, false, true,
+                          workspace, workspace_bytes);
+}
+
+size_t ua_workspace_bytes(const ua_shape *shp, int P)
+{
+    int64_t elems = 0;
+    if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
+    if (empty(shp)) return 0;
+    return (size_t)ua::workspace_bytes(shp->B, shp->S, shp->H / P, (int)shp->d);
+}
+
+int ua_key_split(const ua_shape *shp, int P)
+{
+    int64_t elems = 0;
+    if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
+    if (empty(shp)) return 0;
+    return ua::key_split(shp->B, shp->S, shp->H / P, (int)shp->d);
 }
 
 int attn_ulysses_fused_io(const void *Xq, const void *Xk, const void *Xv, int rank, int P, void *out,
@@ -205,6 +248,7 @@ const char *ua_status_string(int status)
     case UA_ERR_ALIGN: return "a buffer pointer is not 16-byte aligned";
     case UA_ERR_UNSUPPORTED: return "unsupported (d not 64/128, scale not finite and > 0, or shape beyond launch limits)";
     case UA_ERR_HIP: return "the HIP runtime reported an error";
+    case UA_ERR_WORKSPACE: return "workspace smaller than ua_workspace_bytes";
     default: return "unknown status";
     }
 }

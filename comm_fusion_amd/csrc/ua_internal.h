@@ -28,10 +28,13 @@ struct Placement {
 // in_head0 = 0 for the local layout [B][S][Hl][d]; in_heads = H,
 // in_head0 = rank*Hl for the sequence-partitioned input [B][P][S/P][H][d].
 // With a non-null trace, the measurement build runs and fills 4 uint64 per unit.
+// With a non-null workspace (workspace_bytes of the shape, counts zero on
+// entry and again on exit) and no trace, the launch splits each query tile's
+// keys over key_split workgroups.
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t in_heads, int64_t in_head0, int64_t B, int64_t S, int64_t Hl,
                             int d, float scale, const Placement &out, hipStream_t stream,
-                            uint64_t *trace = nullptr);
+                            uint64_t *trace = nullptr, void *workspace = nullptr);
 
 // The attention kernel's epilogue stores alone (closed-form values).
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
@@ -46,7 +49,13 @@ hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t
 hipError_t launch_gather(const Placement &in, int64_t B, int64_t S, int64_t Hl, int d,
                          uint16_t *x_local, hipStream_t stream);
 
-// Work units (one workgroup each) the attention launch uses for this shape.
+// Work units (one workgroup each) the attention launch uses for this shape
+// without a key split (query tiles).
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);
+
+// Workgroups per query tile of a launch given a workspace (1: no split), and
+// the workspace bytes that launch needs (0 when it does not split).
+int key_split(int64_t B, int64_t S, int64_t Hl, int d);
+int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d);
 
 }  // namespace ua

@@ -93,6 +93,12 @@ struct AttnArgs {
     int32_t n_units;
     float scale_log2;  // softmax scale * log2(e)
     uint64_t *trace;   // measurement build only: 4 timestamps per work unit
+    // key split across workgroups (XS builds only): n_split workgroups per
+    // query tile, each on 1/n_split of the keys; their partial results meet
+    // in ws_part, and ws_cnt counts arrivals per query tile
+    int32_t n_split;
+    float *ws_part;
+    unsigned *ws_cnt;
 };
 
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
@@ -100,6 +106,17 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
     f32x2 f = {lo, hi};
     bf16x2 h = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, RNE
     return __builtin_bit_cast(unsigned, h);
+}
+
+// Device-scope relaxed atomic store and load of a float: coherent across the
+// XCDs' L2 caches (sc1), used for the partial results of a key split.
+__device__ __forceinline__ void store_dev(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Lanes l and l+32 hold the same query row (for different keys / columns).
@@ -182,12 +199,18 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
 // per SIMD (and gets that SIMD's whole register file).  RB = 2 (d = 64 only, where the registers allow it): each
 // K or V fragment read from LDS feeds two MFMAs, one per row block, which
 // halves the LDS operand bytes per flop.
+// XS: key split across workgroups, for launches with fewer query tiles than
+// CUs.  Each query tile is shared by a.n_split workgroups, each taking an
+// equal run of the K/V tiles; every one writes its partial O, m and l to
+// a.ws_part, and the last to arrive (an atomic count per query tile) merges
+// all of them in split order -- the same arithmetic whichever workgroup
+// arrives last -- and stores the rows like the unsplit kernel.
 // TRACE: measurement build with the same arithmetic and output, which also
 // records per work unit (in a.trace[4*unit ..]): the 100 MHz constant clock
 // at the start, when every wave has its normalised rows ready (a workgroup
 // barrier), when every wave's epilogue stores have completed (vmcnt(0) and a
 // barrier), and the shader-clock cycles from start to end.
-template <int D, int NW, int RB, int KB, int KS, bool TRACE>
+template <int D, int NW, int RB, int KB, int KS, bool XS, bool TRACE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd(AttnArgs a)
 {
@@ -237,9 +260,12 @@ void attn_fwd(AttnArgs a)
     const int i16 = lane & 15;
     const int half = (lane >> 4) & 1;
 
+    // Unit u = ((b*Hl + h)*n_split + split)*n_qtiles + qt: the units that run
+    // side by side on one XCD read the same keys.
     const int unit = xcd_unit(blockIdx.x, a.n_units);
     const int qt = unit % a.n_qtiles;
-    const int bh = unit / a.n_qtiles;
+    const int split = XS ? unit / a.n_qtiles % a.n_split : 0;
+    const int bh = XS ? unit / a.n_qtiles / a.n_split : unit / a.n_qtiles;
     const int h = bh % a.Hl;
     const int64_t b = bh / a.Hl;
     const int64_t S = a.S;
@@ -249,12 +275,16 @@ void attn_fwd(AttnArgs a)
     // [p*S/P, (p+1)*S/P) back to back), read in place.
     const int rs = a.in_heads * D;  // elements between sequence rows
     const int64_t head = (b * S * a.in_heads + a.in_head0 + h) * D;
-    // Keys of this wave's group: the KS groups split the K/V tiles evenly
-    // (KS = 2 is only launched for an even tile count, so every group runs
-    // the same iterations and barriers, and every group has a full first
-    // tile).  Skv keys starting at key kvbase.
-    const int ntiles = (int)((S + KB - 1) / KB) / KS;
-    const int64_t kvbase = (int64_t)grp * ntiles * KB;
+    // Keys of this wave's group: the KS groups (times the n_split workgroups
+    // of an XS launch) split the K/V tiles evenly (such launches only run
+    // for a tile count divisible by their number of parts, at least 16
+    // tiles per part with a split, so every group runs the same iterations
+    // and barriers, and every group has a full first tile).  Skv keys
+    // starting at key kvbase.
+    const int nparts = XS ? KS * a.n_split : KS;
+    const int part = XS ? split * KS + grp : grp;
+    const int ntiles = (int)((S + KB - 1) / KB) / nparts;
+    const int64_t kvbase = (int64_t)part * ntiles * KB;
     const int64_t Skv = S - kvbase < (int64_t)ntiles * KB ? S - kvbase : (int64_t)ntiles * KB;
     const uint16_t *qh = a.q + head;
     const uint16_t *kh = a.k + head + kvbase * rs;
@@ -741,6 +771,75 @@ void attn_fwd(AttnArgs a)
         }
     }
 
+    // ---- key split across workgroups: publish this workgroup's partial
+    // (group 0's waves hold it, same layout as the key-group hand-off), count
+    // the arrival, and let only the last arrival go on.  It merges the
+    // partials of splits 0 .. n_split-1 in that order from ws_part (its own
+    // included), resets the count for the next call, and stores the rows.
+    // The partials are written and read with device-scope atomic stores and
+    // loads (sc1: coherent across the XCDs' separate L2s without a cache-wide
+    // write-back or invalidate).  A writer waits for its stores to complete
+    // before the arrival is counted, and the last arrival reads only after
+    // its count has returned, so it sees every partial.  Device-scope fences
+    // would add an L2 write-back in every workgroup and an L2 invalidate in
+    // the merging one, needed only for ordinary cached accesses: the merge
+    // makes none, and they slowed the split launch by up to 40%.
+    if constexpr (XS) {
+        constexpr int NX = RB * DB * 16 + 2 * RB;  // floats per lane
+        constexpr int MO = RB * DB * 16;          // m_run at MO + rb, l_run at MO + RB + rb
+        const int64_t tile = (int64_t)bh * a.n_qtiles + qt;
+        const int64_t sstride = (int64_t)NWG * NX * 64;  // floats per split
+        float *const part0 = a.ws_part + tile * a.n_split * sstride + wq * NX * 64 + lane;
+        if (grp == 0) {
+            float *const mine = part0 + split * sstride;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) store_dev(&mine[((rb * DB + db) * 16 + r) * 64], oacc[rb][db][r]);
+                store_dev(&mine[(MO + rb) * 64], m_run[rb]);
+                store_dev(&mine[(MO + RB + rb) * 64], l_run[rb]);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // waits for the partial's stores
+        __syncthreads();  // every wave's stores are complete (and its LDS reads done)
+        typedef __attribute__((address_space(3))) int lds_i32;
+        lds_i32 *const flag = (lds_i32 *)lds_all;
+        if (threadIdx.x == 0) {
+            const unsigned seen = atomicAdd(a.ws_cnt + tile, 1u);
+            const int last = seen == (unsigned)(a.n_split - 1);
+            if (last) atomicExch(a.ws_cnt + tile, 0u);
+            *flag = last;
+        }
+        __syncthreads();
+        if (!*flag) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // partial loads stay after the count
+        if (grp == 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                float m = load_dev(&part0[(MO + rb) * 64]);
+                for (int i = 1; i < a.n_split; ++i) m = fmaxf(m, load_dev(&part0[i * sstride + (MO + rb) * 64]));
+                float l = 0.f;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+                for (int i = 0; i < a.n_split; ++i) {
+                    const float *const pi = part0 + i * sstride;
+                    const float ai = __builtin_amdgcn_exp2f(load_dev(&pi[(MO + rb) * 64]) - m);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            oacc[rb][db][r] = __builtin_fmaf(load_dev(&pi[((rb * DB + db) * 16 + r) * 64]), ai, oacc[rb][db][r]);
+                    l = __builtin_fmaf(load_dev(&pi[(MO + RB + rb) * 64]), ai, l);
+                }
+                l_run[rb] = l;
+            }
+        }
+    }
+
     // ---- epilogue: normalise and store this lane's half of each of its
     // rows straight into the destination slot (region p, row i, head g0 + h).
     float inv[RB];
@@ -900,16 +999,67 @@ LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
     return {8, 1, 64, 1};
 }
 
+// Key split across workgroups for launches with fewer query tiles than CUs
+// (8-wave shapes only): the smallest n in {1, 2, 4, 8} minimising
+// (rounds of n*units over the CUs) * (K/V tiles per part + 8), where the 8
+// stands for a workgroup's fixed cost (prologue, partial write, merge; fitted
+// to measured times of 2-, 4-, 8- and 16-way splits); n must divide the tile
+// count into parts of at least 16 tiles.
+constexpr int64_t kMinSplitTiles = 16;
+constexpr int64_t kSplitFixedTiles = 8;
+
+int key_split_for(const LaunchShape &ls, int64_t B, int64_t S, int64_t Hl)
+{
+    if (ls.nw != 8) return 1;
+    const int64_t units = B * Hl * ((S + ls.rows() - 1) / ls.rows());
+    if (units >= kCUs) return 1;
+    const int64_t nt = (S + ls.kb - 1) / ls.kb;  // K/V tiles over the whole sequence
+    int best = 1;
+    int64_t best_cost = (units + kCUs - 1) / kCUs * (nt / ls.ks + kSplitFixedTiles);
+    for (int n = 2; n <= 8; n *= 2) {
+        if (nt % (ls.ks * n) != 0 || nt / (ls.ks * n) < kMinSplitTiles) continue;
+        const int64_t cost = (units * n + kCUs - 1) / kCUs * (nt / (ls.ks * n) + kSplitFixedTiles);
+        if (cost < best_cost) {
+            best = n;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 template <bool TRACE>
 const void *attention_kernel(int d, const LaunchShape &ls)
 {
     if (d == 128) {
-        if (ls.ks == 2) return (const void *)attn_fwd<128, 8, 1, 32, 2, TRACE>;
-        return ls.nw == 8 ? (const void *)attn_fwd<128, 8, 1, 64, 1, TRACE> : (const void *)attn_fwd<128, 4, 1, 64, 1, TRACE>;
+        if (ls.ks == 2) return (const void *)attn_fwd<128, 8, 1, 32, 2, false, TRACE>;
+        return ls.nw == 8 ? (const void *)attn_fwd<128, 8, 1, 64, 1, false, TRACE>
+                          : (const void *)attn_fwd<128, 4, 1, 64, 1, false, TRACE>;
     }
-    if (ls.ks == 2) return (const void *)attn_fwd<64, 8, 1, 32, 2, TRACE>;
-    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, 1, TRACE>;
-    return ls.nw == 8 ? (const void *)attn_fwd<64, 8, 1, 64, 1, TRACE> : (const void *)attn_fwd<64, 4, 1, 64, 1, TRACE>;
+    if (ls.ks == 2) return (const void *)attn_fwd<64, 8, 1, 32, 2, false, TRACE>;
+    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, 1, false, TRACE>;
+    return ls.nw == 8 ? (const void *)attn_fwd<64, 8, 1, 64, 1, false, TRACE>
+                      : (const void *)attn_fwd<64, 4, 1, 64, 1, false, TRACE>;
+}
+
+// The key-split builds (8-wave shapes only).
+const void *attention_kernel_xs(int d, const LaunchShape &ls)
+{
+    if (d == 128)
+        return ls.ks == 2 ? (const void *)attn_fwd<128, 8, 1, 32, 2, true, false>
+                          : (const void *)attn_fwd<128, 8, 1, 64, 1, true, false>;
+    if (ls.ks == 2) return (const void *)attn_fwd<64, 8, 1, 32, 2, true, false>;
+    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, 1, true, false>;
+    return (const void *)attn_fwd<64, 8, 1, 64, 1, true, false>;
+}
+
+// Workspace of a key-split launch: one uint32 arrival count per query tile
+// (padded to 256 bytes), then per query tile and split the partial results
+// of the NW/KS storing waves, lane-interleaved: (RB*(d/32)*16 + 2*RB) floats
+// per lane.
+int64_t count_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
+int64_t part_floats_per_split(const LaunchShape &ls, int d)
+{
+    return (int64_t)(ls.nw / ls.ks) * (ls.rb * (d / 32) * 16 + 2 * ls.rb) * 64;
 }
 
 }  // namespace
@@ -920,12 +1070,27 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
     return B * Hl * ((S + ls.rows() - 1) / ls.rows());
 }
 
+int key_split(int64_t B, int64_t S, int64_t Hl, int d)
+{
+    return key_split_for(launch_shape(B, S, Hl, d), B, S, Hl);
+}
+
+int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
+{
+    const LaunchShape ls = launch_shape(B, S, Hl, d);
+    const int n = key_split_for(ls, B, S, Hl);
+    if (n == 1) return 0;
+    const int64_t tiles = attention_units(B, S, Hl, d);
+    return count_bytes(tiles) + tiles * n * part_floats_per_split(ls, d) * 4;
+}
+
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t in_heads, int64_t in_head0, int64_t B, int64_t S, int64_t Hl,
                             int d, float scale, const Placement &out, hipStream_t stream,
-                            uint64_t *trace)
+                            uint64_t *trace, void *workspace)
 {
     const LaunchShape ls = launch_shape(B, S, Hl, d);
+    const int n_split = workspace && !trace ? key_split_for(ls, B, S, Hl) : 1;
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -939,8 +1104,19 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.n_units = (int32_t)attention_units(B, S, Hl, d);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.trace = trace;
+    a.n_split = n_split;
+    a.ws_cnt = nullptr;
+    a.ws_part = nullptr;
+    const void *fn;
+    if (n_split > 1) {
+        a.ws_cnt = (unsigned *)workspace;
+        a.ws_part = (float *)((char *)workspace + count_bytes(a.n_units));
+        a.n_units *= n_split;
+        fn = attention_kernel_xs(d, ls);
+    } else {
+        fn = trace ? attention_kernel<true>(d, ls) : attention_kernel<false>(d, ls);
+    }
     void *args[] = {&a};
-    const void *fn = trace ? attention_kernel<true>(d, ls) : attention_kernel<false>(d, ls);
     return hipLaunchKernel(fn, dim3(a.n_units), dim3(64 * ls.nw), args, 0, stream);
 }
 

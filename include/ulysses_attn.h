@@ -29,10 +29,16 @@
  *       (Because the regions are adjacent, this buffer is byte-identical to a
  *       [B][S][H][d] tensor: running every rank fills the full output.)
  *
- * Ownership: the caller allocates and frees every buffer; the library
- * allocates nothing and keeps no state between calls.  A call writes only
+ * Ownership: the caller allocates and frees every buffer (the *_ws calls'
+ * workspace included); the library allocates nothing and keeps no state
+ * between calls.  A call writes only
  * this rank's Hl head slots of `out` (every other slot keeps its bytes).
  * Output buffers must not overlap the inputs.
+ *
+ * The library must run on the process's one HIP runtime: a process that
+ * also uses a copy of the runtime bundled elsewhere (a framework's own
+ * libamdhip64) must load that copy before this library, so that it also
+ * serves this library's dependency (the Python binding does so for torch).
  *
  * Pointers Q, K, V, out, O_local are DEVICE pointers on the current HIP
  * device, 16-byte aligned.  `stream` is a hipStream_t of that device
@@ -74,7 +80,8 @@ enum {
     UA_ERR_RANK = -3,        /* rank outside [0, P)                            */
     UA_ERR_ALIGN = -4,       /* a buffer pointer is not 16-byte aligned        */
     UA_ERR_UNSUPPORTED = -5, /* d not 64/128, scale not finite and > 0, too large */
-    UA_ERR_HIP = -6          /* the HIP runtime reported an error              */
+    UA_ERR_HIP = -6,         /* the HIP runtime reported an error              */
+    UA_ERR_WORKSPACE = -7    /* workspace smaller than ua_workspace_bytes      */
 };
 
 /*
@@ -104,6 +111,41 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P,
  */
 int a2a_permute(const void *O_local, int rank, int P, void *out,
                 const ua_shape *shp, void *stream);
+
+/*
+ * The fused and serial calls with a workspace, for shapes whose query tiles
+ * are fewer than the GPU's 256 CUs (short sequences, few local heads).  The
+ * computation is the same (Fig. 6 of the review page: each output tile has
+ * one owner, which stores it into its destination slot, Fig. 7), except that
+ * the keys of each query tile are split over ua_key_split workgroups: each
+ * writes its partial softmax state (unnormalised O, running max, row sum;
+ * fp32) to the workspace, and the last of them to finish merges the parts in
+ * split order and stores the tile.  Outputs agree with the calls without a
+ * workspace to rounding, not bit-for-bit; attn_serial_ws followed by
+ * a2a_permute writes exactly the bytes attn_ulysses_fused_ws writes.
+ *   workspace: device buffer of at least ua_workspace_bytes(shp, P) bytes,
+ *     16-byte aligned, owned by the caller.  Its first bytes hold arrival
+ *     counts that must be zero before the first call (allocate it zeroed);
+ *     every call leaves them zero again.  Calls that share a workspace must
+ *     not run concurrently (use one stream, or one workspace per stream).
+ *   When ua_workspace_bytes(shp, P) is 0 the shape needs no split: the
+ *   workspace is not touched (it may be NULL) and the call is exactly the
+ *   call without it.  Otherwise a NULL workspace gives UA_ERR_NULL, a
+ *   misaligned one UA_ERR_ALIGN, and workspace_bytes below the requirement
+ *   UA_ERR_WORKSPACE (checked after the other arguments).
+ */
+int attn_ulysses_fused_ws(const void *Q, const void *K, const void *V, int rank, int P,
+                          void *out, const ua_shape *shp, float scale, void *workspace,
+                          size_t workspace_bytes, void *stream);
+int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
+                   void *O_local, const ua_shape *shp, float scale, void *workspace,
+                   size_t workspace_bytes, void *stream);
+/* Workspace bytes the *_ws calls need for this shape (0: no split, or an
+ * invalid or empty shape). */
+size_t ua_workspace_bytes(const ua_shape *shp, int P);
+/* Workgroups sharing each query tile's keys in a *_ws call (1: no split; 0
+ * for an invalid or empty shape). */
+int ua_key_split(const ua_shape *shp, int P);
 
 /*
  * Both exchanges fused.  Fig. 5 steps (a)-(c) of the review page: the

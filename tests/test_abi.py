@@ -37,12 +37,13 @@ def test_library_exports_every_declared_function():
 def test_status_codes_match_header():
     text = open(HEADER).read()
     for name, val in [("UA_OK", 0), ("UA_ERR_NULL", -1), ("UA_ERR_SHAPE", -2), ("UA_ERR_RANK", -3),
-                      ("UA_ERR_ALIGN", -4), ("UA_ERR_UNSUPPORTED", -5), ("UA_ERR_HIP", -6)]:
+                      ("UA_ERR_ALIGN", -4), ("UA_ERR_UNSUPPORTED", -5), ("UA_ERR_HIP", -6),
+                      ("UA_ERR_WORKSPACE", -7)]:
         assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text)
         assert getattr(ua, name) == val
         assert ua.status_string(val) and ua.status_string(val) != "unknown status"
     assert ua.status_string(12345) == "unknown status"
-    assert ua.version() == 10100
+    assert ua.version() == 10200
 
 
 def _fused(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
@@ -60,6 +61,19 @@ def _fused_io(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125):
     return L.attn_ulysses_fused_io(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale, None)
 
 
+W = 0x1000000     # fake workspace address (16-byte aligned)
+
+
+def _fused_ws(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125, ws=W, ws_bytes=1 << 40):
+    return ua.lib().attn_ulysses_fused_ws(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale,
+                                          ws, ws_bytes, None)
+
+
+def _serial_ws(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125, ws=W, ws_bytes=1 << 40):
+    return ua.lib().attn_serial_ws(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale,
+                                   ws, ws_bytes, None)
+
+
 def _permute(shape, rank=0, P=2, src=A, out=O):
     return ua.lib().a2a_permute(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
 
@@ -68,7 +82,7 @@ def _gather(shape, rank=0, P=2, src=A, out=O):
     return ua.lib().a2a_gather(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
 
 
-@pytest.mark.parametrize("call", [_fused, _serial, _fused_io])
+@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _fused_ws, _serial_ws])
 def test_attention_argument_validation(call):
     good = (1, 64, 4, 64)
     assert ua.lib().attn_ulysses_fused(A, B_, C, 0, 2, O, None, 0.1, None) == ua.UA_ERR_NULL
@@ -95,7 +109,7 @@ def test_attention_argument_validation(call):
     assert call((0, 1, 1 << 17, 128), P=1) == ua.UA_OK  # Hl*d = 2^24 is allowed
 
 
-@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _permute, _gather])
+@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _fused_ws, _serial_ws, _permute, _gather])
 def test_empty_calls_succeed_without_touching_memory(call):
     copy = call in (_permute, _gather)
     assert call((0, 64, 4, 64), src=0, out=0) == ua.UA_OK if copy else \
@@ -175,3 +189,48 @@ def test_work_units():
     assert ua.work_units(3, 129, 9, 64, 3) == 3 * 3 * 2
     assert ua.work_units(0, 64, 4, 64, 2) == 0
     assert ua.work_units(1, 63, 4, 64, 2) == 0                 # invalid shape
+
+
+def test_key_split_choice_and_workspace_size():
+    # video_dit, mixed and tiny fill the CUs (or are too short): no split
+    assert ua.key_split(1, 65536, 40, 128, 8) == 1 and ua.workspace_bytes(1, 65536, 40, 128, 8) == 0
+    assert ua.key_split(2, 32768, 24, 64, 4) == 1 and ua.workspace_bytes(2, 32768, 24, 64, 4) == 0
+    assert ua.key_split(1, 512, 4, 64, 2) == 1 and ua.workspace_bytes(1, 512, 4, 64, 2) == 0
+    # dit_long: 192 query tiles of 256 rows, 256 key tiles of 64: n = 4 gives
+    # 768 workgroups = 3 rounds of 64 + 8 tiles (216) against 1 round of 264
+    assert ua.key_split(1, 16384, 24, 128, 8) == 4
+    tiles, nx = 192, 4 * 16 + 2                     # floats per lane: O^T blocks, m, l
+    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 768 + tiles * 4 * 8 * nx * 64 * 4
+    # dit_image: 96 tiles of 128 rows, two key groups of 64 tiles of 32 keys:
+    # n = 2 (1 round of 40) beats n = 1 (72) and n = 4 (2 rounds of 24); n = 8
+    # would leave parts of 8 tiles
+    assert ua.key_split(1, 4096, 24, 128, 8) == 2
+    assert ua.workspace_bytes(1, 4096, 24, 128, 8) == 512 + 96 * 2 * 4 * nx * 64 * 4
+    # d = 64 with two row blocks per wave: nx = 2 * (2 * 16) + 4
+    assert ua.work_units(1, 16384, 48, 64, 8) == 6 * 32 and ua.key_split(1, 16384, 48, 64, 8) == 4
+    assert ua.workspace_bytes(1, 16384, 48, 64, 8) == 768 + 192 * 4 * 8 * 68 * 64 * 4
+    # 160 tiles of 256 rows over 320 key tiles: n = 8 (5 rounds of 48) beats
+    # n = 4 (3 rounds of 88); at 8192 keys n = 4 and n = 8 tie (120), the
+    # smaller wins
+    assert ua.key_split(1, 20480, 16, 128, 8) == 8
+    assert ua.key_split(1, 8192, 40, 64, 8) == 4
+    # a one-wave-per-SIMD launch (odd 32-key tile count) never splits
+    assert ua.key_split(1, 127 * 32, 8, 128, 8) == 1
+    assert ua.key_split(0, 64, 4, 64, 2) == 0 and ua.key_split(1, 63, 4, 64, 2) == 0
+    assert ua.workspace_bytes(1, 63, 4, 64, 2) == 0
+
+
+def test_workspace_validation():
+    shape = (1, 16384, 24, 128)                   # needs a workspace at P = 8
+    need = ua.workspace_bytes(*shape, 8)
+    for call in (_fused_ws, _serial_ws):
+        assert call(shape, P=8, ws=0) == ua.UA_ERR_NULL
+        assert call(shape, P=8, ws=W + 8) == ua.UA_ERR_ALIGN
+        assert call(shape, P=8, ws_bytes=need - 1) == ua.UA_ERR_WORKSPACE
+        assert call(shape, P=8, ws_bytes=0) == ua.UA_ERR_WORKSPACE
+        # the other arguments are checked first
+        assert call(shape, P=8, q=0, ws=0) == ua.UA_ERR_NULL
+        assert call(shape, P=8, rank=8, ws_bytes=0) == ua.UA_ERR_RANK
+        assert call(shape, P=8, out=O + 2, ws_bytes=0) == ua.UA_ERR_ALIGN
+        # empty calls need nothing
+        assert call((0, 16384, 24, 128), P=8, q=0, k=0, v=0, out=0, ws=0, ws_bytes=0) == ua.UA_OK

@@ -70,3 +70,20 @@ def test_tensors_of_one_call_must_share_a_device():
         _binding._stream(s, a, a)
     assert _binding._stream(s, b, b) == 1234
     assert _binding._stream(5678, a, a) == 5678      # a raw handle is taken as given
+
+
+def test_library_shares_the_hip_runtime_that_torch_loads():
+    # Loading the library through the binding before torch has been imported
+    # must still leave one HIP runtime in the process (torch's): two copies
+    # would make torch's pointers and streams invalid in the library's calls.
+    import subprocess
+    import sys
+    code = ("import comm_fusion_amd as ua; ua.lib(); import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "paths = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+            "print(len(paths)); print(paths)\n")
+    root = __import__("os").path.dirname(__import__("os").path.dirname(__import__("os").path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    lines = out.stdout.strip().splitlines()
+    assert lines[0] == "1", lines

@@ -75,3 +75,35 @@ def test_fused_calls_replay_from_a_graph():
     others = np.delete(fused.view(torch.int16).view(B, S, H, d).cpu().numpy(),
                        np.s_[rank * Hl:(rank + 1) * Hl], axis=2)
     assert np.all(others.view(np.uint16) == SENTINEL_BITS)
+
+
+def test_key_split_call_replays_from_a_graph():
+    # The workspace's arrival counts are reset by the kernel itself, so every
+    # replay (no memset in the graph) returns the eager call's bits.
+    import torch
+    B, S, H, P, rank, d = 2, 2048, 8, 2, 1, 64
+    assert ua.key_split(B, S, H, d, P) > 1
+    q, k, v = (to_dev(x).view(B, S, H // P, d) for x in make_qkv(B, S, H // P, d, 31))
+    ws = ua.new_workspace(B, S, H, d, P, q.device)
+    out = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused_ws(q, k, v, rank, P, out, ws)
+    torch.cuda.synchronize()
+    ref = out.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ua.attn_ulysses_fused_ws(q, k, v, rank, P, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ua.attn_ulysses_fused_ws(q, k, v, rank, P, out, ws)
+    sentinel = SENTINEL_BITS - 0x10000 if SENTINEL_BITS >= 0x8000 else SENTINEL_BITS
+    for _ in range(3):
+        out.view(torch.int16).fill_(sentinel)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
