@@ -341,13 +341,19 @@ def main():
             X[:, :, lo:hi] = t.view(w.B, w.S, w.Hl, w.d)
             xs.append(X)
         g_loc = [torch.empty_like(q) for _ in range(3)]
-        fns["fused_io"] = lambda: ua.attn_ulysses_fused_io(xs[0], xs[1], xs[2], w.rank, w.P, dest)
+        if n_split > 1:
+            fns["fused_io"] = lambda: ua.attn_ulysses_fused_io_ws(xs[0], xs[1], xs[2], w.rank, w.P, dest, ws)
+        else:
+            fns["fused_io"] = lambda: ua.attn_ulysses_fused_io(xs[0], xs[1], xs[2], w.rank, w.P, dest)
         fns["gather"] = lambda: ua.a2a_gather(xs[0], w.rank, w.P, g_loc[0])
 
         def serial_io():
             for X, L in zip(xs, g_loc):
                 ua.a2a_gather(X, w.rank, w.P, L)
-            ua.attn_serial(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local)
+            if n_split > 1:
+                ua.attn_serial_ws(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local, ws)
+            else:
+                ua.attn_serial(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local)
             perm()
         fns["serial_io"] = serial_io
 

@@ -15,6 +15,7 @@ Names and arguments follow the C calls:
   a2a_gather(X, rank, P, X_local, stream=None)
   attn_ulysses_fused_ws(Q, K, V, rank, P, out, workspace, scale=None, stream=None)
   attn_serial_ws(Q, K, V, rank, P, O_local, workspace, scale=None, stream=None)
+  attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, out, workspace, scale=None, stream=None)
   workspace_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
   new_workspace(B, S, H, d, P, device)  (a zeroed uint8 tensor, or None)
 and, for measurement only,
@@ -29,6 +30,7 @@ Tensors are torch tensors on the GPU: Q, K, V, O_local bfloat16
 from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # noqa: F401
                        UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_OK, UAError,
                        a2a_gather, a2a_permute, attn_serial, attn_serial_ws, attn_ulysses_fused,
-                       attn_ulysses_fused_io, attn_ulysses_fused_trace, attn_ulysses_fused_ws,
+                       attn_ulysses_fused_io, attn_ulysses_fused_io_ws, attn_ulysses_fused_trace,
+                       attn_ulysses_fused_ws,
                        dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
                        new_workspace, status_string, version, work_units, workspace_bytes)

@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.attn_ulysses_fused_ws.restype = i
     L.attn_serial_ws.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp, sz, vp]
     L.attn_serial_ws.restype = i
+    L.attn_ulysses_fused_io_ws.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp, sz, vp]
+    L.attn_ulysses_fused_io_ws.restype = i
     L.ua_workspace_bytes.argtypes = [sp, i]
     L.ua_workspace_bytes.restype = sz
     L.ua_key_split.argtypes = [sp, i]
@@ -309,3 +311,19 @@ def attn_serial_ws(Q, K, V, rank, P, O_local, workspace, scale=None, stream=None
                               ctypes.byref(shp), scale, wp, wb, _stream(stream, Q, K, V, O_local, workspace))
     if st != UA_OK:
         raise UAError("attn_serial_ws", st)
+
+
+def attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, out, workspace, scale=None, stream=None):
+    """attn_ulysses_fused_io with a workspace (see new_workspace)."""
+    shp = _seq_shape(Xq, P)
+    n = shp.B * shp.S * shp.H * shp.d
+    for nm, t in (("Xq", Xq), ("Xk", Xk), ("Xv", Xv)):
+        _check_bf16(nm, t, n)
+    _check_bf16("out", out, n)
+    wp, wb = _ws(workspace)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_ulysses_fused_io_ws(_ptr(Xq), _ptr(Xk), _ptr(Xv), int(rank), int(P), _ptr(out),
+                                        ctypes.byref(shp), scale, wp, wb,
+                                        _stream(stream, Xq, Xk, Xv, out, workspace))
+    if st != UA_OK:
+        raise UAError("attn_ulysses_fused_io_ws", st)

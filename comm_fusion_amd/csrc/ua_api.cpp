@@ -157,6 +157,14 @@ int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
                           workspace, workspace_bytes);
 }
 
+int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int rank, int P, void *out,
+                             const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    return attention_call(Xq, Xk, Xv, rank, P, out, shp, scale, stream, true, nullptr, false, true, true,
+                          workspace, workspace_bytes);
+}
+
 size_t ua_workspace_bytes(const ua_shape *shp, int P)
 {
     int64_t elems = 0;

@@ -140,6 +140,12 @@ int attn_ulysses_fused_ws(const void *Q, const void *K, const void *V, int rank,
 int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
                    void *O_local, const ua_shape *shp, float scale, void *workspace,
                    size_t workspace_bytes, void *stream);
+/* attn_ulysses_fused_io (below) with a workspace, as the two calls above:
+ * bit-identical to a2a_gather of Xq, Xk, Xv followed by
+ * attn_ulysses_fused_ws on the same workspace. */
+int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int rank, int P,
+                             void *out, const ua_shape *shp, float scale, void *workspace,
+                             size_t workspace_bytes, void *stream);
 /* Workspace bytes the *_ws calls need for this shape (0: no split, or an
  * invalid or empty shape). */
 size_t ua_workspace_bytes(const ua_shape *shp, int P);

@@ -74,6 +74,11 @@ def _serial_ws(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125, ws=W, ws_
                                    ws, ws_bytes, None)
 
 
+def _fused_io_ws(shape, rank=0, P=2, q=A, k=B_, v=C, out=O, scale=0.125, ws=W, ws_bytes=1 << 40):
+    return ua.lib().attn_ulysses_fused_io_ws(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale,
+                                             ws, ws_bytes, None)
+
+
 def _permute(shape, rank=0, P=2, src=A, out=O):
     return ua.lib().a2a_permute(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
 
@@ -82,7 +87,7 @@ def _gather(shape, rank=0, P=2, src=A, out=O):
     return ua.lib().a2a_gather(src, rank, P, out, ctypes.byref(Shape(*shape)), None)
 
 
-@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _fused_ws, _serial_ws])
+@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _fused_ws, _serial_ws, _fused_io_ws])
 def test_attention_argument_validation(call):
     good = (1, 64, 4, 64)
     assert ua.lib().attn_ulysses_fused(A, B_, C, 0, 2, O, None, 0.1, None) == ua.UA_ERR_NULL
@@ -109,7 +114,8 @@ def test_attention_argument_validation(call):
     assert call((0, 1, 1 << 17, 128), P=1) == ua.UA_OK  # Hl*d = 2^24 is allowed
 
 
-@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _fused_ws, _serial_ws, _permute, _gather])
+@pytest.mark.parametrize("call", [_fused, _serial, _fused_io, _fused_ws, _serial_ws, _fused_io_ws,
+                                  _permute, _gather])
 def test_empty_calls_succeed_without_touching_memory(call):
     copy = call in (_permute, _gather)
     assert call((0, 64, 4, 64), src=0, out=0) == ua.UA_OK if copy else \
@@ -223,7 +229,7 @@ def test_key_split_choice_and_workspace_size():
 def test_workspace_validation():
     shape = (1, 16384, 24, 128)                   # needs a workspace at P = 8
     need = ua.workspace_bytes(*shape, 8)
-    for call in (_fused_ws, _serial_ws):
+    for call in (_fused_ws, _serial_ws, _fused_io_ws):
         assert call(shape, P=8, ws=0) == ua.UA_ERR_NULL
         assert call(shape, P=8, ws=W + 8) == ua.UA_ERR_ALIGN
         assert call(shape, P=8, ws_bytes=need - 1) == ua.UA_ERR_WORKSPACE

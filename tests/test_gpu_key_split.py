@@ -145,3 +145,20 @@ def test_split_and_unsplit_calls_agree_to_rounding():
     b4 = b.reshape(B, S, H, d)[:, :, rank * Hl:(rank + 1) * Hl]
     diff = np.abs(a4 - b4)
     assert diff.max() <= 4 * 2.0 ** -8 * max(np.abs(b4).max(), 1e-3), diff.max()
+
+
+def test_fused_io_with_key_split_equals_gather_then_fused():
+    # Both exchanges fused, split launch: reading this rank's heads in place
+    # from [B][P][S/P][H][d] gives the bytes of a2a_gather + attn_ulysses_fused_ws.
+    B, S, H, P, rank, d = 1, 4096, 24, 8, 6, 128
+    assert ua.key_split(B, S, H, d, P) == 2
+    Xq, Xk, Xv = (_dev4(x) for x in make_qkv(B, S, H, d, 50))
+    ws = ua.new_workspace(B, S, H, d, P, Xq.device)
+    io = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, io, ws)
+    loc = [empty_bf16(B * S * (H // P) * d).view(B, S, H // P, d) for _ in range(3)]
+    for X, L in zip((Xq, Xk, Xv), loc):
+        ua.a2a_gather(X, rank, P, L)
+    ref = _fused_ws(*loc, rank, P, H, ws)
+    np.testing.assert_array_equal(to_host_bits(io), ref)
+    check_dest_layout(ref, B, S, H, d, P, rank)
