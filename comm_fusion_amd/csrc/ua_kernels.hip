@@ -774,8 +774,8 @@ void attn_fwd(AttnArgs a)
     // ---- key split across workgroups: publish this workgroup's partial
     // (group 0's waves hold it, same layout as the key-group hand-off), count
     // the arrival, and let only the last arrival go on.  It merges the
-    // partials of splits 0 .. n_split-1 in that order from ws_part (its own
-    // included), resets the count for the next call, and stores the rows.
+    // partials of splits 0 .. n_split-1 in that order, resets the count for
+    // the next call, and stores the rows.
     // The partials are written and read with device-scope atomic stores and
     // loads (sc1: coherent across the XCDs' separate L2s without a cache-wide
     // write-back or invalidate).  A writer waits for its stores to complete
@@ -815,27 +815,54 @@ void attn_fwd(AttnArgs a)
         __syncthreads();
         if (!*flag) return;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // partial loads stay after the count
+        // Merge in split order with a running max: part 0 is taken as is, and
+        // part i rescales the sum so far by 2^(M - M') and adds its own by
+        // 2^(m_i - M').  The order is fixed, so the result does not depend on
+        // which workgroup merges; that workgroup takes its own part from
+        // registers (the same values it stored) and loads each other part's
+        // O, m and l in one batch, one memory round trip per part.
         if (grp == 0) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                float m = load_dev(&part0[(MO + rb) * 64]);
-                for (int i = 1; i < a.n_split; ++i) m = fmaxf(m, load_dev(&part0[i * sstride + (MO + rb) * 64]));
-                float l = 0.f;
+                f32x16 own[DB];
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+                for (int db = 0; db < DB; ++db) own[db] = oacc[rb][db];
+                float M = 0.f, L = 0.f;
                 for (int i = 0; i < a.n_split; ++i) {
-                    const float *const pi = part0 + i * sstride;
-                    const float ai = __builtin_amdgcn_exp2f(load_dev(&pi[(MO + rb) * 64]) - m);
+                    f32x16 oi[DB];
+                    float mi, li;
+                    if (i == split) {
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
+                        for (int db = 0; db < DB; ++db) oi[db] = own[db];
+                        mi = m_run[rb];
+                        li = l_run[rb];
+                    } else {
+                        const float *const pi = part0 + i * sstride;
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            oacc[rb][db][r] = __builtin_fmaf(load_dev(&pi[((rb * DB + db) * 16 + r) * 64]), ai, oacc[rb][db][r]);
-                    l = __builtin_fmaf(load_dev(&pi[(MO + RB + rb) * 64]), ai, l);
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oi[db][r] = load_dev(&pi[((rb * DB + db) * 16 + r) * 64]);
+                        mi = load_dev(&pi[(MO + rb) * 64]);
+                        li = load_dev(&pi[(MO + RB + rb) * 64]);
+                    }
+                    if (i == 0) {
+#pragma unroll
+                        for (int db = 0; db < DB; ++db) oacc[rb][db] = oi[db];
+                        M = mi;
+                        L = li;
+                    } else {
+                        const float Mn = fmaxf(M, mi);
+                        const float aa = __builtin_amdgcn_exp2f(M - Mn), ai = __builtin_amdgcn_exp2f(mi - Mn);
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                oacc[rb][db][r] = __builtin_fmaf(oi[db][r], ai, oacc[rb][db][r] * aa);
+                        L = __builtin_fmaf(li, ai, L * aa);
+                        M = Mn;
+                    }
                 }
-                l_run[rb] = l;
+                l_run[rb] = L;
             }
         }
     }
