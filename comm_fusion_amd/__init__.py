@@ -16,7 +16,7 @@ Names and arguments follow the C calls:
   attn_ulysses_fused_ws(Q, K, V, rank, P, out, workspace, scale=None, stream=None)
   attn_serial_ws(Q, K, V, rank, P, O_local, workspace, scale=None, stream=None)
   attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, out, workspace, scale=None, stream=None)
-  workspace_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
+  workspace_bytes(B, S, H, d, P), workspace_count_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
   new_workspace(B, S, H, d, P, device)  (a zeroed uint8 tensor, or None)
 and, for measurement only,
   attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None)
@@ -33,4 +33,5 @@ from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # no
                        attn_ulysses_fused_io, attn_ulysses_fused_io_ws, attn_ulysses_fused_trace,
                        attn_ulysses_fused_ws,
                        dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
-                       new_workspace, status_string, version, work_units, workspace_bytes)
+                       new_workspace, status_string, version, work_units, workspace_bytes,
+                       workspace_count_bytes)

@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.attn_ulysses_fused_io_ws.restype = i
     L.ua_workspace_bytes.argtypes = [sp, i]
     L.ua_workspace_bytes.restype = sz
+    L.ua_workspace_count_bytes.argtypes = [sp, i]
+    L.ua_workspace_count_bytes.restype = sz
     L.ua_key_split.argtypes = [sp, i]
     L.ua_key_split.restype = i
     _lib = L
@@ -260,6 +262,11 @@ def epilogue_store_only(B, S, H, d, rank, P, out, stream=None):
 def workspace_bytes(B, S, H, d, P) -> int:
     """Workspace bytes the *_ws calls need for this shape (0: no key split)."""
     return int(lib().ua_workspace_bytes(ctypes.byref(Shape(B, S, H, d)), int(P)))
+
+
+def workspace_count_bytes(B, S, H, d, P) -> int:
+    """Leading workspace bytes that hold the arrival counts (zero between calls)."""
+    return int(lib().ua_workspace_count_bytes(ctypes.byref(Shape(B, S, H, d)), int(P)))
 
 
 def key_split(B, S, H, d, P) -> int:

@@ -173,6 +173,14 @@ size_t ua_workspace_bytes(const ua_shape *shp, int P)
     return (size_t)ua::workspace_bytes(shp->B, shp->S, shp->H / P, (int)shp->d);
 }
 
+size_t ua_workspace_count_bytes(const ua_shape *shp, int P)
+{
+    int64_t elems = 0;
+    if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
+    if (empty(shp)) return 0;
+    return (size_t)ua::workspace_count_bytes(shp->B, shp->S, shp->H / P, (int)shp->d);
+}
+
 int ua_key_split(const ua_shape *shp, int P)
 {
     int64_t elems = 0;

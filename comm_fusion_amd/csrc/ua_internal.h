@@ -57,5 +57,7 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);
 // the workspace bytes that launch needs (0 when it does not split).
 int key_split(int64_t B, int64_t S, int64_t Hl, int d);
 int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d);
+// Leading bytes of that workspace that hold the arrival counts.
+int64_t workspace_count_bytes(int64_t B, int64_t S, int64_t Hl, int d);
 
 }  // namespace ua

@@ -275,16 +275,24 @@ void attn_fwd(AttnArgs a)
     // [p*S/P, (p+1)*S/P) back to back), read in place.
     const int rs = a.in_heads * D;  // elements between sequence rows
     const int64_t head = (b * S * a.in_heads + a.in_head0 + h) * D;
-    // Keys of this wave's group: the KS groups (times the n_split workgroups
-    // of an XS launch) split the K/V tiles evenly (such launches only run
-    // for a tile count divisible by their number of parts, at least 16
-    // tiles per part with a split, so every group runs the same iterations
-    // and barriers, and every group has a full first tile).  Skv keys
-    // starting at key kvbase.
-    const int nparts = XS ? KS * a.n_split : KS;
-    const int part = XS ? split * KS + grp : grp;
-    const int ntiles = (int)((S + KB - 1) / KB) / nparts;
-    const int64_t kvbase = (int64_t)part * ntiles * KB;
+    // Keys of this wave's group: the KS groups split the K/V tiles evenly
+    // (KS = 2 only runs for an even tile count, so both groups run the same
+    // iterations and barriers).  In an XS launch, split s of n first takes
+    // units [s*U/n, (s+1)*U/n) of the U = tiles/KS units of KS tiles each
+    // (parts of at least 8 units), and its groups halve that run.  Every
+    // group has a full first tile.  Skv keys starting at key kvbase.
+    const int nt_all = (int)((S + KB - 1) / KB);
+    int ntiles;
+    int64_t kvbase;
+    if constexpr (XS) {
+        const int U = nt_all / KS;
+        const int u0 = (int)((int64_t)split * U / a.n_split), u1 = (int)((int64_t)(split + 1) * U / a.n_split);
+        ntiles = u1 - u0;
+        kvbase = (int64_t)(u0 * KS + grp * ntiles) * KB;
+    } else {
+        ntiles = nt_all / KS;
+        kvbase = (int64_t)grp * ntiles * KB;
+    }
     const int64_t Skv = S - kvbase < (int64_t)ntiles * KB ? S - kvbase : (int64_t)ntiles * KB;
     const uint16_t *qh = a.q + head;
     const uint16_t *kh = a.k + head + kvbase * rs;
@@ -1026,31 +1034,53 @@ LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
     return {8, 1, 64, 1};
 }
 
-// Key split across workgroups for launches with fewer query tiles than CUs
-// (8-wave shapes only): the smallest n in {1, 2, 4, 8} minimising
-// (rounds of n*units over the CUs) * (K/V tiles per part + 8), where the 8
-// stands for a workgroup's fixed cost (prologue, partial write, merge; fitted
-// to measured times of 2-, 4-, 8- and 16-way splits); n must divide the tile
-// count into parts of at least 16 tiles.
-constexpr int64_t kMinSplitTiles = 16;
-constexpr int64_t kSplitFixedTiles = 8;
+// Key split across workgroups for launches with fewer query tiles than CUs:
+// the launch shape and the number n of workgroups per query tile.  The
+// candidates are the plain call's shape and, where that shape uses 128-row
+// units (fewer than 128 units of 256 rows), the 256-row shape on 64-key
+// tiles; only 8-wave shapes split.  Each candidate with n in 1 .. 4 costs
+// (rounds of n * units over the 256 CUs) * (keys one wave processes + 512
+// + 128 (n - 1)): 512 keys' worth of time stand for a workgroup's fixed cost
+// (prologue, partial write, count) and 128 for each part the merging
+// workgroup loads (one memory round trip), both fitted to measured 2- to
+// 16-way splits of dit_image and dit_long.  Parts hold at least 8 units of
+// KS tiles.  The cheapest wins, ties going to the smaller n and then to the
+// plain call's shape; n = 1 means the plain launch (the other shape only
+// competes with a split).
+constexpr int kSplitMaxN = 4;
+constexpr int64_t kMinSplitUnits = 8;
+constexpr int64_t kSplitFixedKeys = 512;
+constexpr int64_t kSplitPartKeys = 128;
 
-int key_split_for(const LaunchShape &ls, int64_t B, int64_t S, int64_t Hl)
+struct SplitPlan {
+    LaunchShape ls;
+    int n;
+};
+
+SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    if (ls.nw != 8) return 1;
-    const int64_t units = B * Hl * ((S + ls.rows() - 1) / ls.rows());
-    if (units >= kCUs) return 1;
-    const int64_t nt = (S + ls.kb - 1) / ls.kb;  // K/V tiles over the whole sequence
-    int best = 1;
-    int64_t best_cost = (units + kCUs - 1) / kCUs * (nt / ls.ks + kSplitFixedTiles);
-    for (int n = 2; n <= 8; n *= 2) {
-        if (nt % (ls.ks * n) != 0 || nt / (ls.ks * n) < kMinSplitTiles) continue;
-        const int64_t cost = (units * n + kCUs - 1) / kCUs * (nt / (ls.ks * n) + kSplitFixedTiles);
-        if (cost < best_cost) {
-            best = n;
-            best_cost = cost;
+    const LaunchShape plain = launch_shape(B, S, Hl, d);
+    const auto units = [&](const LaunchShape &ls) { return B * Hl * ((S + ls.rows() - 1) / ls.rows()); };
+    SplitPlan best = {plain, 1};
+    if (units(plain) >= kCUs) return best;
+    const int64_t U0 = (S + plain.kb - 1) / plain.kb / plain.ks;
+    int64_t best_cost = (units(plain) + kCUs - 1) / kCUs * (U0 * plain.kb + kSplitFixedKeys);
+    LaunchShape cands[2] = {plain, {8, 1, 64, 1}};
+    const int ncand = plain.rows() == 128 ? 2 : 1;
+    for (int n = 1; n <= kSplitMaxN; ++n)
+        for (int c = 0; c < ncand; ++c) {
+            const LaunchShape &ls = cands[c];
+            if (ls.nw != 8 || (n == 1 && c > 0)) continue;
+            const int64_t U = (S + ls.kb - 1) / ls.kb / ls.ks;  // units of ks tiles
+            if (n > 1 && U / n < kMinSplitUnits) continue;
+            const int64_t cost = (units(ls) * n + kCUs - 1) / kCUs *
+                                 ((U + n - 1) / n * ls.kb + kSplitFixedKeys + kSplitPartKeys * (n - 1));
+            if (cost < best_cost) {
+                best = {ls, n};
+                best_cost = cost;
+            }
         }
-    }
+    if (best.n == 1) best.ls = plain;
     return best;
 }
 
@@ -1097,18 +1127,21 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
     return B * Hl * ((S + ls.rows() - 1) / ls.rows());
 }
 
-int key_split(int64_t B, int64_t S, int64_t Hl, int d)
+int key_split(int64_t B, int64_t S, int64_t Hl, int d) { return split_plan(B, S, Hl, d).n; }
+
+int64_t workspace_count_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    return key_split_for(launch_shape(B, S, Hl, d), B, S, Hl);
+    const SplitPlan sp = split_plan(B, S, Hl, d);
+    if (sp.n == 1) return 0;
+    return count_bytes(B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows()));
 }
 
 int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const LaunchShape ls = launch_shape(B, S, Hl, d);
-    const int n = key_split_for(ls, B, S, Hl);
-    if (n == 1) return 0;
-    const int64_t tiles = attention_units(B, S, Hl, d);
-    return count_bytes(tiles) + tiles * n * part_floats_per_split(ls, d) * 4;
+    const SplitPlan sp = split_plan(B, S, Hl, d);
+    if (sp.n == 1) return 0;
+    const int64_t tiles = B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows());
+    return count_bytes(tiles) + tiles * sp.n * part_floats_per_split(sp.ls, d) * 4;
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -1116,8 +1149,9 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             int d, float scale, const Placement &out, hipStream_t stream,
                             uint64_t *trace, void *workspace)
 {
-    const LaunchShape ls = launch_shape(B, S, Hl, d);
-    const int n_split = workspace && !trace ? key_split_for(ls, B, S, Hl) : 1;
+    const SplitPlan sp = workspace && !trace ? split_plan(B, S, Hl, d) : SplitPlan{launch_shape(B, S, Hl, d), 1};
+    const LaunchShape ls = sp.ls;
+    const int n_split = sp.n;
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -1128,7 +1162,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.in_heads = (int32_t)in_heads;
     a.in_head0 = (int32_t)in_head0;
     a.n_qtiles = (int32_t)((S + ls.rows() - 1) / ls.rows());
-    a.n_units = (int32_t)attention_units(B, S, Hl, d);
+    a.n_units = (int32_t)(B * Hl * a.n_qtiles);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.trace = trace;
     a.n_split = n_split;

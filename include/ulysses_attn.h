@@ -124,9 +124,10 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
  * workspace to rounding, not bit-for-bit; attn_serial_ws followed by
  * a2a_permute writes exactly the bytes attn_ulysses_fused_ws writes.
  *   workspace: device buffer of at least ua_workspace_bytes(shp, P) bytes,
- *     16-byte aligned, owned by the caller.  Its first bytes hold arrival
- *     counts that must be zero before the first call (allocate it zeroed);
- *     every call leaves them zero again.  Calls that share a workspace must
+ *     16-byte aligned, owned by the caller.  Its first
+ *     ua_workspace_count_bytes(shp, P) bytes hold arrival counts that must be
+ *     zero before the first call (allocate it zeroed); every call leaves them
+ *     zero again.  The rest holds partial results.  Calls that share a workspace must
  *     not run concurrently (use one stream, or one workspace per stream).
  *   When ua_workspace_bytes(shp, P) is 0 the shape needs no split: the
  *   workspace is not touched (it may be NULL) and the call is exactly the
@@ -149,6 +150,10 @@ int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int
 /* Workspace bytes the *_ws calls need for this shape (0: no split, or an
  * invalid or empty shape). */
 size_t ua_workspace_bytes(const ua_shape *shp, int P);
+/* Leading bytes of that workspace holding the arrival counts: the part that
+ * must be zero before a call (every call leaves it zero); 0 when the shape
+ * needs no workspace. */
+size_t ua_workspace_count_bytes(const ua_shape *shp, int P);
 /* Workgroups sharing each query tile's keys in a *_ws call (1: no split; 0
  * for an invalid or empty shape). */
 int ua_key_split(const ua_shape *shp, int P);

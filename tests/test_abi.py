@@ -198,30 +198,45 @@ def test_work_units():
 
 
 def test_key_split_choice_and_workspace_size():
+    # The rule: for launches with fewer query tiles than the 256 CUs, the
+    # plain call's shape (and, where that uses 128-row units, the 256-row one
+    # on 64-key tiles) with n in 1..4 workgroups per tile, costing
+    # rounds(n * tiles / 256) * (keys one wave processes + 512 + 128 (n - 1));
+    # parts of at least 8 units of KS tiles.
     # video_dit, mixed and tiny fill the CUs (or are too short): no split
     assert ua.key_split(1, 65536, 40, 128, 8) == 1 and ua.workspace_bytes(1, 65536, 40, 128, 8) == 0
     assert ua.key_split(2, 32768, 24, 64, 4) == 1 and ua.workspace_bytes(2, 32768, 24, 64, 4) == 0
     assert ua.key_split(1, 512, 4, 64, 2) == 1 and ua.workspace_bytes(1, 512, 4, 64, 2) == 0
-    # dit_long: 192 query tiles of 256 rows, 256 key tiles of 64: n = 4 gives
-    # 768 workgroups = 3 rounds of 64 + 8 tiles (216) against 1 round of 264
+    nx = 4 * 16 + 2                                 # floats per lane at d = 128: O^T blocks, m, l
+    # dit_long: 192 tiles of 256 rows over 256 key tiles of 64: n = 4 gives
+    # 768 workgroups = 3 rounds of 64 tiles: 3 * (4096 + 512 + 384) against
+    # 1 * (16384 + 512) and 2 * (8192 + 640)
     assert ua.key_split(1, 16384, 24, 128, 8) == 4
-    tiles, nx = 192, 4 * 16 + 2                     # floats per lane: O^T blocks, m, l
-    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 768 + tiles * 4 * 8 * nx * 64 * 4
-    # dit_image: 96 tiles of 128 rows, two key groups of 64 tiles of 32 keys:
-    # n = 2 (1 round of 40) beats n = 1 (72) and n = 4 (2 rounds of 24); n = 8
-    # would leave parts of 8 tiles
+    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 768 + 192 * 4 * 8 * nx * 64 * 4
+    # dit_image: 96 tiles of 128 rows (two key groups of 4 waves on 32-key
+    # tiles): n = 2 (1024 + 640) beats n = 1 (2048 + 512), and the 256-row
+    # shape on 64-key tiles split 4 ways (1024 + 896)
     assert ua.key_split(1, 4096, 24, 128, 8) == 2
     assert ua.workspace_bytes(1, 4096, 24, 128, 8) == 512 + 96 * 2 * 4 * nx * 64 * 4
-    # d = 64 with two row blocks per wave: nx = 2 * (2 * 16) + 4
+    assert ua.workspace_count_bytes(1, 4096, 24, 128, 8) == 512           # 96 uint32 counts, padded
+    assert ua.workspace_count_bytes(1, 16384, 24, 128, 8) == 768          # 192 counts
+    assert ua.workspace_count_bytes(1, 65536, 40, 128, 8) == 0
+    # d = 64 with two row blocks per wave (nx = 2 * (2 * 16) + 4), 192 tiles
     assert ua.work_units(1, 16384, 48, 64, 8) == 6 * 32 and ua.key_split(1, 16384, 48, 64, 8) == 4
     assert ua.workspace_bytes(1, 16384, 48, 64, 8) == 768 + 192 * 4 * 8 * 68 * 64 * 4
-    # 160 tiles of 256 rows over 320 key tiles: n = 8 (5 rounds of 48) beats
-    # n = 4 (3 rounds of 88); at 8192 keys n = 4 and n = 8 tie (120), the
-    # smaller wins
-    assert ua.key_split(1, 20480, 16, 128, 8) == 8
-    assert ua.key_split(1, 8192, 40, 64, 8) == 4
-    # a one-wave-per-SIMD launch (odd 32-key tile count) never splits
-    assert ua.key_split(1, 127 * 32, 8, 128, 8) == 1
+    # 160 tiles over 128 key tiles: n = 3 (480 workgroups, 2 rounds of 43
+    # tiles: 2 * (2752 + 768)) beats n = 4 (3 rounds) and n = 1; the parts
+    # are 42, 43, 43
+    assert ua.key_split(1, 8192, 40, 64, 8) == 3
+    # one head of 4096 keys: 32 tiles of 128 rows split 4 ways, 16 pairs of
+    # 32-key tiles per workgroup (4 storing waves per workgroup)
+    assert ua.key_split(1, 4096, 8, 128, 8) == 4
+    assert ua.workspace_bytes(1, 4096, 8, 128, 8) == 256 + 32 * 4 * 4 * nx * 64 * 4
+    # an odd 32-key tile count puts the plain call on one wave per SIMD (4-wave
+    # workgroups of 128 rows); the split runs the 8-wave 256-row shape instead:
+    # 16 tiles split 4 ways over 64 key tiles (the last one half full)
+    assert ua.key_split(1, 127 * 32, 8, 128, 8) == 4
+    assert ua.workspace_bytes(1, 127 * 32, 8, 128, 8) == 256 + 16 * 4 * 8 * nx * 64 * 4
     assert ua.key_split(0, 64, 4, 64, 2) == 0 and ua.key_split(1, 63, 4, 64, 2) == 0
     assert ua.workspace_bytes(1, 63, 4, 64, 2) == 0
 

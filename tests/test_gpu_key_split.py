@@ -39,11 +39,6 @@ def _fused_ws(q, k, v, rank, P, H, ws):
     return to_host_bits(dest)
 
 
-def _count_bytes(B, S, H, d, P):
-    tiles = ua.work_units(B, S, H, d, P)
-    return (tiles * 4 + 255) // 256 * 256
-
-
 def _check_split_call(Q, K, V, H, P, rank, rows, what):
     B, S, Hl, d = Q.shape
     q, k, v = _dev4(Q), _dev4(K), _dev4(V)
@@ -63,7 +58,7 @@ def _check_split_call(Q, K, V, H, P, rank, rows, what):
     np.testing.assert_array_equal(to_host_bits(dest2), dest)
     # the counts were reset: a second call on the same workspace, same bits
     np.testing.assert_array_equal(_fused_ws(q, k, v, rank, P, H, ws), dest)
-    cnt = ws[:_count_bytes(B, S, H, d, P)].cpu().numpy()
+    cnt = ws[:ua.workspace_count_bytes(B, S, H, d, P)].cpu().numpy()
     assert not cnt.any(), "arrival counts not reset"
     return err
 
@@ -71,11 +66,12 @@ def _check_split_call(Q, K, V, H, P, rank, rows, what):
 # B, S, H, P, rank, d, seed, expected key split
 SPLIT_CASES = [
     (1, 4096, 24, 8, 3, 128, 41, 2),   # the DiT-image shape: two key groups of 4 waves, 96 tiles
-    (1, 8176, 8, 8, 2, 128, 42, 4),    # ragged: last query tile 112 rows, last key tile 16 keys
+    (1, 8176, 8, 8, 2, 128, 42, 4),    # ragged: last query tile 112 rows, last key tile 16 keys; key groups
     (2, 2048, 8, 2, 1, 64, 43, 2),     # d = 64 with key groups, B = 2
-    (1, 8192, 40, 8, 0, 64, 44, 4),    # d = 64, one row block per wave on 64-key tiles
-    (1, 20480, 16, 8, 3, 128, 49, 8),  # 8 parts of 40 key tiles, 1280 workgroups
+    (1, 8192, 40, 8, 0, 64, 44, 3),    # d = 64, one row block per wave, parts of 42, 43, 43 tiles
     (1, 16384, 48, 8, 1, 64, 45, 4),   # d = 64, two row blocks per wave
+    (1, 3584, 8, 8, 1, 64, 51, 4),     # d = 64 with key groups, parts of 14 tile pairs
+    (1, 4064, 8, 8, 6, 128, 52, 4),    # plain call on one wave per SIMD; split on the 8-wave shape, ragged last key tile
 ]
 
 
