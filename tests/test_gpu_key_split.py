@@ -158,3 +158,29 @@ def test_fused_io_with_key_split_equals_gather_then_fused():
     ref = _fused_ws(*loc, rank, P, H, ws)
     np.testing.assert_array_equal(to_host_bits(io), ref)
     check_dest_layout(ref, B, S, H, d, P, rank)
+
+
+def test_all_ranks_with_key_split_compose_to_full_multihead_attention():
+    # One global [B][S][H][d] problem; every rank runs its split call on its
+    # head slice into one destination, each rank with its own workspace.
+    # Afterwards no sentinel remains and sampled rows of every global head
+    # match the oracle.
+    import torch
+    B, S, H, P, d = 1, 4096, 16, 8, 128
+    Hl = H // P
+    assert ua.key_split(B, S, H, d, P) > 1
+    Qg, Kg, Vg = make_qkv(B, S, H, d, 53)
+    dest = sentinel_buffer(B * S * H * d)
+    for r in range(P):
+        sl = np.s_[:, :, r * Hl:(r + 1) * Hl]
+        q, k, v = (_dev4(np.ascontiguousarray(t[sl])) for t in (Qg, Kg, Vg))
+        ws = ua.new_workspace(B, S, H, d, P, q.device)
+        ua.attn_ulysses_fused_ws(q, k, v, r, P, dest, ws)
+    torch.cuda.synchronize()
+    got = to_host_bits(dest)
+    assert not np.any(got == np.uint16(0x7FD5))
+    w = Workload("t", B, S, H, 1, 0, d, 53, sampled=True)
+    rows = sampled_rows(w, n_per_head=32)
+    ref = oracle.attn_rows(Qg, Kg, Vg, 1.0 / math.sqrt(d), rows)     # rows of all H heads
+    offs = oracle.dest_offsets(rows, B, S, H, d, 1, 0)                # P = 1: plain [B][S][H][d]
+    assert_close(bits_to_f64(got[offs[:, None] + np.arange(d)[None, :]]), ref, "all ranks, split")
