@@ -127,7 +127,8 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
  *     16-byte aligned, owned by the caller.  Its first
  *     ua_workspace_count_bytes(shp, P) bytes hold arrival counts that must be
  *     zero before the first call (allocate it zeroed); every call leaves them
- *     zero again.  The rest holds partial results.  Calls that share a workspace must
+ *     zero again.  The rest holds partial results.  So one workspace serves
+ *     every shape whose ua_workspace_bytes does not exceed its size.  Calls that share a workspace must
  *     not run concurrently (use one stream, or one workspace per stream).
  *   When ua_workspace_bytes(shp, P) is 0 the shape needs no split: the
  *   workspace is not touched (it may be NULL) and the call is exactly the
