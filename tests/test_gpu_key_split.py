@@ -184,3 +184,23 @@ def test_all_ranks_with_key_split_compose_to_full_multihead_attention():
     ref = oracle.attn_rows(Qg, Kg, Vg, 1.0 / math.sqrt(d), rows)     # rows of all H heads
     offs = oracle.dest_offsets(rows, B, S, H, d, 1, 0)                # P = 1: plain [B][S][H][d]
     assert_close(bits_to_f64(got[offs[:, None] + np.arange(d)[None, :]]), ref, "all ranks, split")
+
+
+def test_one_workspace_serves_shapes_in_turn():
+    # A workspace sized for the larger shape serves a smaller one in between:
+    # every call leaves the arrival counts at zero, and the results equal the
+    # same calls on fresh workspaces, bit for bit.
+    big = WORKLOADS["dit_long"]
+    small = WORKLOADS["dit_image"]
+    assert ua.workspace_bytes(big.B, big.S, big.H, big.d, big.P) >= \
+        ua.workspace_bytes(small.B, small.S, small.H, small.d, small.P) > 0
+    ins = {}
+    for w in (big, small):
+        ins[w.name] = [_dev4(x) for x in workload_qkv(w)]
+    shared = ua.new_workspace(big.B, big.S, big.H, big.d, big.P, ins[big.name][0].device)
+    got = []
+    for w in (big, small, big):
+        got.append(_fused_ws(*ins[w.name], w.rank, w.P, w.H, shared))
+    for w, g in zip((big, small, big), got):
+        fresh = ua.new_workspace(w.B, w.S, w.H, w.d, w.P, ins[w.name][0].device)
+        np.testing.assert_array_equal(g, _fused_ws(*ins[w.name], w.rank, w.P, w.H, fresh))
