@@ -1081,6 +1081,8 @@ SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d)
             }
         }
     if (best.n == 1) best.ls = plain;
+    // every split plan has fewer query tiles than CUs (the other candidate has
+    // fewer tiles than the plain shape), so its counts fit kCountBytes
     return best;
 }
 
@@ -1110,10 +1112,12 @@ const void *attention_kernel_xs(int d, const LaunchShape &ls)
 }
 
 // Workspace of a key-split launch: one uint32 arrival count per query tile
-// (padded to 256 bytes), then per query tile and split the partial results
-// of the NW/KS storing waves, lane-interleaved: (RB*(d/32)*16 + 2*RB) floats
-// per lane.
-int64_t count_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
+// in a region of fixed size (a split only runs for fewer query tiles than
+// CUs), then per query tile and split the partial results of the NW/KS
+// storing waves, lane-interleaved: (RB*(d/32)*16 + 2*RB) floats per lane.
+// The fixed count region keeps every shape's counts clear of every other
+// shape's partials, so one workspace (counts zero) serves any shape it fits.
+constexpr int64_t kCountBytes = kCUs * 4;
 int64_t part_floats_per_split(const LaunchShape &ls, int d)
 {
     return (int64_t)(ls.nw / ls.ks) * (ls.rb * (d / 32) * 16 + 2 * ls.rb) * 64;
@@ -1132,8 +1136,7 @@ int key_split(int64_t B, int64_t S, int64_t Hl, int d) { return split_plan(B, S,
 int64_t workspace_count_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 {
     const SplitPlan sp = split_plan(B, S, Hl, d);
-    if (sp.n == 1) return 0;
-    return count_bytes(B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows()));
+    return sp.n == 1 ? 0 : kCountBytes;
 }
 
 int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
@@ -1141,7 +1144,7 @@ int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
     const SplitPlan sp = split_plan(B, S, Hl, d);
     if (sp.n == 1) return 0;
     const int64_t tiles = B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows());
-    return count_bytes(tiles) + tiles * sp.n * part_floats_per_split(sp.ls, d) * 4;
+    return kCountBytes + tiles * sp.n * part_floats_per_split(sp.ls, d) * 4;
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -1171,7 +1174,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     const void *fn;
     if (n_split > 1) {
         a.ws_cnt = (unsigned *)workspace;
-        a.ws_part = (float *)((char *)workspace + count_bytes(a.n_units));
+        a.ws_part = (float *)((char *)workspace + kCountBytes);
         a.n_units *= n_split;
         fn = attention_kernel_xs(d, ls);
     } else {

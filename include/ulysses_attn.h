@@ -125,10 +125,11 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
  * a2a_permute writes exactly the bytes attn_ulysses_fused_ws writes.
  *   workspace: device buffer of at least ua_workspace_bytes(shp, P) bytes,
  *     16-byte aligned, owned by the caller.  Its first
- *     ua_workspace_count_bytes(shp, P) bytes hold arrival counts that must be
- *     zero before the first call (allocate it zeroed); every call leaves them
- *     zero again.  The rest holds partial results.  So one workspace serves
- *     every shape whose ua_workspace_bytes does not exceed its size.  Calls that share a workspace must
+ *     ua_workspace_count_bytes(shp, P) bytes (1024 for every shape that
+ *     splits) hold arrival counts that must be zero before the first call
+ *     (allocate it zeroed); every call leaves them zero again.  The rest
+ *     holds partial results.  So one workspace serves every shape whose
+ *     ua_workspace_bytes does not exceed its size.  Calls that share a workspace must
  *     not run concurrently (use one stream, or one workspace per stream).
  *   When ua_workspace_bytes(shp, P) is 0 the shape needs no split: the
  *   workspace is not touched (it may be NULL) and the call is exactly the
@@ -152,8 +153,8 @@ int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int
  * invalid or empty shape). */
 size_t ua_workspace_bytes(const ua_shape *shp, int P);
 /* Leading bytes of that workspace holding the arrival counts: the part that
- * must be zero before a call (every call leaves it zero); 0 when the shape
- * needs no workspace. */
+ * must be zero before a call (every call leaves it zero); 1024 for every
+ * shape that splits, 0 when the shape needs no workspace. */
 size_t ua_workspace_count_bytes(const ua_shape *shp, int P);
 /* Workgroups sharing each query tile's keys in a *_ws call (1: no split; 0
  * for an invalid or empty shape). */

@@ -212,18 +212,18 @@ def test_key_split_choice_and_workspace_size():
     # 768 workgroups = 3 rounds of 64 tiles: 3 * (4096 + 512 + 384) against
     # 1 * (16384 + 512) and 2 * (8192 + 640)
     assert ua.key_split(1, 16384, 24, 128, 8) == 4
-    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 768 + 192 * 4 * 8 * nx * 64 * 4
+    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 1024 + 192 * 4 * 8 * nx * 64 * 4
     # dit_image: 96 tiles of 128 rows (two key groups of 4 waves on 32-key
     # tiles): n = 2 (1024 + 640) beats n = 1 (2048 + 512), and the 256-row
     # shape on 64-key tiles split 4 ways (1024 + 896)
     assert ua.key_split(1, 4096, 24, 128, 8) == 2
-    assert ua.workspace_bytes(1, 4096, 24, 128, 8) == 512 + 96 * 2 * 4 * nx * 64 * 4
-    assert ua.workspace_count_bytes(1, 4096, 24, 128, 8) == 512           # 96 uint32 counts, padded
-    assert ua.workspace_count_bytes(1, 16384, 24, 128, 8) == 768          # 192 counts
+    assert ua.workspace_bytes(1, 4096, 24, 128, 8) == 1024 + 96 * 2 * 4 * nx * 64 * 4
+    assert ua.workspace_count_bytes(1, 4096, 24, 128, 8) == 1024   # counts of up to 256 query tiles
+    assert ua.workspace_count_bytes(1, 16384, 24, 128, 8) == 1024
     assert ua.workspace_count_bytes(1, 65536, 40, 128, 8) == 0
     # d = 64 with two row blocks per wave (nx = 2 * (2 * 16) + 4), 192 tiles
     assert ua.work_units(1, 16384, 48, 64, 8) == 6 * 32 and ua.key_split(1, 16384, 48, 64, 8) == 4
-    assert ua.workspace_bytes(1, 16384, 48, 64, 8) == 768 + 192 * 4 * 8 * 68 * 64 * 4
+    assert ua.workspace_bytes(1, 16384, 48, 64, 8) == 1024 + 192 * 4 * 8 * 68 * 64 * 4
     # 160 tiles over 128 key tiles: n = 3 (480 workgroups, 2 rounds of 43
     # tiles: 2 * (2752 + 768)) beats n = 4 (3 rounds) and n = 1; the parts
     # are 42, 43, 43
@@ -231,12 +231,12 @@ def test_key_split_choice_and_workspace_size():
     # one head of 4096 keys: 32 tiles of 128 rows split 4 ways, 16 pairs of
     # 32-key tiles per workgroup (4 storing waves per workgroup)
     assert ua.key_split(1, 4096, 8, 128, 8) == 4
-    assert ua.workspace_bytes(1, 4096, 8, 128, 8) == 256 + 32 * 4 * 4 * nx * 64 * 4
+    assert ua.workspace_bytes(1, 4096, 8, 128, 8) == 1024 + 32 * 4 * 4 * nx * 64 * 4
     # an odd 32-key tile count puts the plain call on one wave per SIMD (4-wave
     # workgroups of 128 rows); the split runs the 8-wave 256-row shape instead:
     # 16 tiles split 4 ways over 64 key tiles (the last one half full)
     assert ua.key_split(1, 127 * 32, 8, 128, 8) == 4
-    assert ua.workspace_bytes(1, 127 * 32, 8, 128, 8) == 256 + 16 * 4 * 8 * nx * 64 * 4
+    assert ua.workspace_bytes(1, 127 * 32, 8, 128, 8) == 1024 + 16 * 4 * 8 * nx * 64 * 4
     assert ua.key_split(0, 64, 4, 64, 2) == 0 and ua.key_split(1, 63, 4, 64, 2) == 0
     assert ua.workspace_bytes(1, 63, 4, 64, 2) == 0
 
