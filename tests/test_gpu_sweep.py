@@ -1,4 +1,4 @@
-"""Seeded sweep of random valid shapes through every entry point (GPU).
+"""Seeded sweeps of random valid shapes through every entry point (GPU).
 
 Shapes are drawn once from a fixed seed: batch 1-3, P in {1, 2, 3, 4, 5, 8}
 (any rank), S a multiple of P that is mostly ragged against the 64-key and
@@ -6,7 +6,8 @@ Shapes are drawn once from a fixed seed: batch 1-3, P in {1, 2, 3, 4, 5, 8}
 8-wave launch.  Each shape is checked against the oracle on sampled rows, for
 the exact destination layout, and for bit equality between the fused call,
 the serial attention + permute, and the fused call on sequence-partitioned
-inputs.
+inputs.  A third sweep does the same for the calls with a workspace on shapes
+whose query tiles are few enough for a key split.
 """
 import math
 
@@ -78,6 +79,27 @@ def sweep_shapes_b(n=16, seed=2027):
 SHAPES_B = sweep_shapes_b()
 
 
+def sweep_shapes_split(n=12, seed=2028):
+    """Shapes for the calls with a workspace (key split): few query tiles
+    (B*Hl*ceil(S/128) <= 96) and 2048-12000 keys, mostly ragged against the
+    tiles, both head dims, any P and rank; bounded like the other sweeps."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        P = int(rng.choice([1, 2, 3, 4, 8]))
+        Hl = int(rng.choice([1, 2, 3]))
+        B = int(rng.integers(1, 3))
+        S = P * int(rng.integers(2048 // P, 1 + 12000 // P))
+        if B * Hl * -(-S // 128) > 96 or B * S * Hl * P * d > 2.5e7:
+            continue
+        out.append((B, S, Hl * P, P, int(rng.integers(0, P)), d, 500 + len(out)))
+    return out
+
+
+SHAPES_SPLIT = sweep_shapes_split()
+
+
 def _dev(a):
     return to_dev(a).view(*a.shape)
 
@@ -106,3 +128,32 @@ def test_sweep(B, S, H, P, rank, d, seed):
     offs = oracle.dest_offsets(rows, B, S, H, d, P, rank)
     assert np.all(offs >= 0)
     assert_close(bits_to_f64(got[offs[:, None] + np.arange(d)[None, :]]), ref, "sweep %r" % ((B, S, H, P, rank, d),))
+
+
+@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SHAPES_SPLIT)
+def test_sweep_key_split(B, S, H, P, rank, d, seed):
+    import torch
+    Hl = H // P
+    assert ua.key_split(B, S, H, d, P) > 1
+    Xq, Xk, Xv = make_qkv(B, S, H, d, seed)
+    Q, K, V = (oracle.gather(x, H, P, rank) for x in (Xq, Xk, Xv))
+    q, k, v = _dev(Q), _dev(K), _dev(V)
+    ws = ua.new_workspace(B, S, H, d, P, q.device)
+    n = B * S * H * d
+    fused, io, serial = sentinel_buffer(n), sentinel_buffer(n), sentinel_buffer(n)
+    o_local = empty_bf16(Q.size).view(B, S, Hl, d)
+    ua.attn_ulysses_fused_ws(q, k, v, rank, P, fused, ws)
+    ua.attn_ulysses_fused_io_ws(_dev(Xq), _dev(Xk), _dev(Xv), rank, P, io, ws)
+    ua.attn_serial_ws(q, k, v, rank, P, o_local, ws)
+    ua.a2a_permute(o_local, rank, P, serial)
+    torch.cuda.synchronize()
+    got = to_host_bits(fused)
+    check_dest_layout(got, B, S, H, d, P, rank)
+    np.testing.assert_array_equal(got, to_host_bits(serial))
+    np.testing.assert_array_equal(got, to_host_bits(io))
+    assert not ws[:ua.workspace_count_bytes(B, S, H, d, P)].cpu().numpy().any()
+    rows = sampled_rows(Workload("sweep", B, S, H, P, rank, d, seed, sampled=True), n_per_head=16)
+    ref = oracle.attn_rows(Q, K, V, 1.0 / math.sqrt(d), rows)
+    offs = oracle.dest_offsets(rows, B, S, H, d, P, rank)
+    assert_close(bits_to_f64(got[offs[:, None] + np.arange(d)[None, :]]), ref,
+                 "split sweep %r" % ((B, S, H, P, rank, d),))
