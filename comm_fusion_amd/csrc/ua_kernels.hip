@@ -94,8 +94,8 @@ struct AttnArgs {
     float scale_log2;  // softmax scale * log2(e)
     uint64_t *trace;   // measurement build only: 4 timestamps per work unit
     // key split across workgroups (XS builds only): n_split workgroups per
-    // query tile, each on 1/n_split of the keys; their partial results meet
-    // in ws_part, and ws_cnt counts arrivals per query tile
+    // query tile, each on a run of about 1/n_split of the keys; their partial
+    // results meet in ws_part, and ws_cnt counts arrivals per query tile
     int32_t n_split;
     float *ws_part;
     unsigned *ws_cnt;
@@ -200,8 +200,9 @@ __device__ __forceinline__ int xcd_unit(int bid, int n)
 // K or V fragment read from LDS feeds two MFMAs, one per row block, which
 // halves the LDS operand bytes per flop.
 // XS: key split across workgroups, for launches with fewer query tiles than
-// CUs.  Each query tile is shared by a.n_split workgroups, each taking an
-// equal run of the K/V tiles; every one writes its partial O, m and l to
+// CUs.  Each query tile is shared by a.n_split workgroups, each taking a
+// run of the K/V tiles (the runs differ by at most one unit of KS tiles);
+// every one writes its partial O, m and l to
 // a.ws_part, and the last to arrive (an atomic count per query tile) merges
 // all of them in split order -- the same arithmetic whichever workgroup
 // arrives last -- and stores the rows like the unsplit kernel.
