@@ -1035,8 +1035,10 @@ LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
     return {8, 1, 64, 1};
 }
 
-// Key split across workgroups for launches with fewer query tiles than CUs:
-// the launch shape and the number n of workgroups per query tile.  The
+// Key split across workgroups for launches with fewer than 1024 query tiles
+// (four rounds over the CUs), where too few tiles or a last round that fills
+// the CUs poorly leave CUs idle: the launch shape and the number n of
+// workgroups per query tile.  The
 // candidates are the plain call's shape and, where that shape uses 128-row
 // units (fewer than 128 units of 256 rows), the 256-row shape on 64-key
 // tiles; only 8-wave shapes split.  Each candidate with n in 1 .. 4 costs
@@ -1049,6 +1051,8 @@ LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
 // plain call's shape; n = 1 means the plain launch (the other shape only
 // competes with a split).
 constexpr int kSplitMaxN = 4;
+constexpr int64_t kSplitMaxTiles = 1024;
+constexpr int64_t kCountBytes = kSplitMaxTiles * 4;
 constexpr int64_t kMinSplitUnits = 8;
 constexpr int64_t kSplitFixedKeys = 512;
 constexpr int64_t kSplitPartKeys = 128;
@@ -1063,7 +1067,7 @@ SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d)
     const LaunchShape plain = launch_shape(B, S, Hl, d);
     const auto units = [&](const LaunchShape &ls) { return B * Hl * ((S + ls.rows() - 1) / ls.rows()); };
     SplitPlan best = {plain, 1};
-    if (units(plain) >= kCUs) return best;
+    if (units(plain) >= kSplitMaxTiles) return best;
     const int64_t U0 = (S + plain.kb - 1) / plain.kb / plain.ks;
     int64_t best_cost = (units(plain) + kCUs - 1) / kCUs * (U0 * plain.kb + kSplitFixedKeys);
     LaunchShape cands[2] = {plain, {8, 1, 64, 1}};
@@ -1082,8 +1086,9 @@ SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d)
             }
         }
     if (best.n == 1) best.ls = plain;
-    // every split plan has fewer query tiles than CUs (the other candidate has
-    // fewer tiles than the plain shape), so its counts fit kCountBytes
+    // every split plan has fewer than kSplitMaxTiles query tiles (the other
+    // candidate has fewer tiles than the plain shape), so its counts fit
+    // kCountBytes
     return best;
 }
 
@@ -1113,12 +1118,12 @@ const void *attention_kernel_xs(int d, const LaunchShape &ls)
 }
 
 // Workspace of a key-split launch: one uint32 arrival count per query tile
-// in a region of fixed size (a split only runs for fewer query tiles than
-// CUs), then per query tile and split the partial results of the NW/KS
-// storing waves, lane-interleaved: (RB*(d/32)*16 + 2*RB) floats per lane.
-// The fixed count region keeps every shape's counts clear of every other
-// shape's partials, so one workspace (counts zero) serves any shape it fits.
-constexpr int64_t kCountBytes = kCUs * 4;
+// in a region of fixed size (a split only runs for fewer than
+// kSplitMaxTiles query tiles), then per query tile and split the partial
+// results of the NW/KS storing waves, lane-interleaved: (RB*(d/32)*16 +
+// 2*RB) floats per lane.  The fixed count region keeps every shape's counts
+// clear of every other shape's partials, so one workspace (counts zero)
+// serves any shape it fits.
 int64_t part_floats_per_split(const LaunchShape &ls, int d)
 {
     return (int64_t)(ls.nw / ls.ks) * (ls.rb * (d / 32) * 16 + 2 * ls.rb) * 64;

@@ -114,7 +114,8 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
 
 /*
  * The fused and serial calls with a workspace, for shapes whose query tiles
- * are fewer than the GPU's 256 CUs (short sequences, few local heads).  The
+ * leave CUs idle: fewer tiles than the GPU's 256 CUs (short sequences, few
+ * local heads), or a last round over the CUs that few tiles fill.  The
  * computation is the same (Fig. 6 of the review page: each output tile has
  * one owner, which stores it into its destination slot, Fig. 7), except that
  * the keys of each query tile are split over ua_key_split workgroups: each
@@ -125,7 +126,7 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
  * a2a_permute writes exactly the bytes attn_ulysses_fused_ws writes.
  *   workspace: device buffer of at least ua_workspace_bytes(shp, P) bytes,
  *     16-byte aligned, owned by the caller.  Its first
- *     ua_workspace_count_bytes(shp, P) bytes (1024 for every shape that
+ *     ua_workspace_count_bytes(shp, P) bytes (4096 for every shape that
  *     splits) hold arrival counts that must be zero before the first call
  *     (allocate it zeroed); every call leaves them zero again.  The rest
  *     holds partial results.  So one workspace serves every shape whose
@@ -153,7 +154,7 @@ int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int
  * invalid or empty shape). */
 size_t ua_workspace_bytes(const ua_shape *shp, int P);
 /* Leading bytes of that workspace holding the arrival counts: the part that
- * must be zero before a call (every call leaves it zero); 1024 for every
+ * must be zero before a call (every call leaves it zero); 4096 for every
  * shape that splits, 0 when the shape needs no workspace. */
 size_t ua_workspace_count_bytes(const ua_shape *shp, int P);
 /* Workgroups sharing each query tile's keys in a *_ws call (1: no split; 0

@@ -198,12 +198,12 @@ def test_work_units():
 
 
 def test_key_split_choice_and_workspace_size():
-    # The rule: for launches with fewer query tiles than the 256 CUs, the
+    # The rule: for launches with fewer than 1024 query tiles, the
     # plain call's shape (and, where that uses 128-row units, the 256-row one
     # on 64-key tiles) with n in 1..4 workgroups per tile, costing
     # rounds(n * tiles / 256) * (keys one wave processes + 512 + 128 (n - 1));
     # parts of at least 8 units of KS tiles.
-    # video_dit, mixed and tiny fill the CUs (or are too short): no split
+    # video_dit (1280 tiles), mixed (3 full rounds) and tiny (too short): no split
     assert ua.key_split(1, 65536, 40, 128, 8) == 1 and ua.workspace_bytes(1, 65536, 40, 128, 8) == 0
     assert ua.key_split(2, 32768, 24, 64, 4) == 1 and ua.workspace_bytes(2, 32768, 24, 64, 4) == 0
     assert ua.key_split(1, 512, 4, 64, 2) == 1 and ua.workspace_bytes(1, 512, 4, 64, 2) == 0
@@ -212,18 +212,18 @@ def test_key_split_choice_and_workspace_size():
     # 768 workgroups = 3 rounds of 64 tiles: 3 * (4096 + 512 + 384) against
     # 1 * (16384 + 512) and 2 * (8192 + 640)
     assert ua.key_split(1, 16384, 24, 128, 8) == 4
-    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 1024 + 192 * 4 * 8 * nx * 64 * 4
+    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 4096 + 192 * 4 * 8 * nx * 64 * 4
     # dit_image: 96 tiles of 128 rows (two key groups of 4 waves on 32-key
     # tiles): n = 2 (1024 + 640) beats n = 1 (2048 + 512), and the 256-row
     # shape on 64-key tiles split 4 ways (1024 + 896)
     assert ua.key_split(1, 4096, 24, 128, 8) == 2
-    assert ua.workspace_bytes(1, 4096, 24, 128, 8) == 1024 + 96 * 2 * 4 * nx * 64 * 4
-    assert ua.workspace_count_bytes(1, 4096, 24, 128, 8) == 1024   # counts of up to 256 query tiles
-    assert ua.workspace_count_bytes(1, 16384, 24, 128, 8) == 1024
+    assert ua.workspace_bytes(1, 4096, 24, 128, 8) == 4096 + 96 * 2 * 4 * nx * 64 * 4
+    assert ua.workspace_count_bytes(1, 4096, 24, 128, 8) == 4096   # counts of up to 1024 query tiles
+    assert ua.workspace_count_bytes(1, 16384, 24, 128, 8) == 4096
     assert ua.workspace_count_bytes(1, 65536, 40, 128, 8) == 0
     # d = 64 with two row blocks per wave (nx = 2 * (2 * 16) + 4), 192 tiles
     assert ua.work_units(1, 16384, 48, 64, 8) == 6 * 32 and ua.key_split(1, 16384, 48, 64, 8) == 4
-    assert ua.workspace_bytes(1, 16384, 48, 64, 8) == 1024 + 192 * 4 * 8 * 68 * 64 * 4
+    assert ua.workspace_bytes(1, 16384, 48, 64, 8) == 4096 + 192 * 4 * 8 * 68 * 64 * 4
     # 160 tiles over 128 key tiles: n = 3 (480 workgroups, 2 rounds of 43
     # tiles: 2 * (2752 + 768)) beats n = 4 (3 rounds) and n = 1; the parts
     # are 42, 43, 43
@@ -231,12 +231,18 @@ def test_key_split_choice_and_workspace_size():
     # one head of 4096 keys: 32 tiles of 128 rows split 4 ways, 16 pairs of
     # 32-key tiles per workgroup (4 storing waves per workgroup)
     assert ua.key_split(1, 4096, 8, 128, 8) == 4
-    assert ua.workspace_bytes(1, 4096, 8, 128, 8) == 1024 + 32 * 4 * 4 * nx * 64 * 4
+    assert ua.workspace_bytes(1, 4096, 8, 128, 8) == 4096 + 32 * 4 * 4 * nx * 64 * 4
+    # 320 tiles (1.25 rounds) of video_dit's heads at 16384 keys: n = 4, five
+    # full rounds of 64 key tiles (5 * 4992) against 2 * 16896; at 32768 keys
+    # 640 tiles (2.5 rounds) split 2 ways
+    assert ua.key_split(1, 16384, 40, 128, 8) == 4
+    assert ua.key_split(1, 32768, 40, 128, 8) == 2
+    assert ua.workspace_bytes(1, 32768, 40, 128, 8) == 4096 + 640 * 2 * 8 * nx * 64 * 4
     # an odd 32-key tile count puts the plain call on one wave per SIMD (4-wave
     # workgroups of 128 rows); the split runs the 8-wave 256-row shape instead:
     # 16 tiles split 4 ways over 64 key tiles (the last one half full)
     assert ua.key_split(1, 127 * 32, 8, 128, 8) == 4
-    assert ua.workspace_bytes(1, 127 * 32, 8, 128, 8) == 1024 + 16 * 4 * 8 * nx * 64 * 4
+    assert ua.workspace_bytes(1, 127 * 32, 8, 128, 8) == 4096 + 16 * 4 * 8 * nx * 64 * 4
     assert ua.key_split(0, 64, 4, 64, 2) == 0 and ua.key_split(1, 63, 4, 64, 2) == 0
     assert ua.workspace_bytes(1, 63, 4, 64, 2) == 0
 

@@ -72,6 +72,8 @@ SPLIT_CASES = [
     (1, 16384, 48, 8, 1, 64, 45, 4),   # d = 64, two row blocks per wave
     (1, 3584, 8, 8, 1, 64, 51, 4),     # d = 64 with key groups, parts of 14 tile pairs
     (1, 4064, 8, 8, 6, 128, 52, 4),    # plain call on one wave per SIMD; split on the 8-wave shape, ragged last key tile
+    (1, 16384, 40, 8, 7, 128, 54, 4),  # 320 tiles (1.25 rounds unsplit): five full rounds
+    (1, 32768, 40, 8, 2, 128, 55, 2),  # 640 tiles (2.5 rounds unsplit): five full rounds
 ]
 
 
@@ -111,9 +113,10 @@ def test_workloads_with_key_split_at_full_size(name):
 
 
 def test_workspace_call_without_split_is_the_plain_call():
-    # video_dit-like head count at a short length fills the CUs: no split, the
-    # workspace is not needed and the output is the plain call's, bit for bit.
-    for (B, S, H, P, rank, d) in [(1, 512, 4, 2, 0, 64), (1, 4096, 160, 8, 7, 128)]:
+    # Shapes the plain launch already serves best (too short; 256 query tiles,
+    # one full round over the CUs): no split, the workspace is not needed and
+    # the output is the plain call's, bit for bit.
+    for (B, S, H, P, rank, d) in [(1, 512, 4, 2, 0, 64), (1, 4096, 128, 8, 7, 128)]:
         assert ua.key_split(B, S, H, d, P) == 1 and ua.workspace_bytes(B, S, H, d, P) == 0
         Q, K, V = make_qkv(B, S, H // P, d, 47)
         q, k, v = _dev4(Q), _dev4(K), _dev4(V)
