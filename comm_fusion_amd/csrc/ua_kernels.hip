@@ -785,14 +785,15 @@ void attn_fwd(AttnArgs a)
     // the arrival, and let only the last arrival go on.  It merges the
     // partials of splits 0 .. n_split-1 in that order, resets the count for
     // the next call, and stores the rows.
-    // The partials are written and read with device-scope atomic stores and
-    // loads (sc1: coherent across the XCDs' separate L2s without a cache-wide
-    // write-back or invalidate).  A writer waits for its stores to complete
-    // before the arrival is counted, and the last arrival reads only after
-    // its count has returned, so it sees every partial.  Device-scope fences
-    // would add an L2 write-back in every workgroup and an L2 invalidate in
-    // the merging one, needed only for ordinary cached accesses: the merge
-    // makes none, and they slowed the split launch by up to 40%.
+    // Ordering: the waves' partial stores, a workgroup barrier, then thread
+    // 0's device-scope release add; in the merging workgroup, thread 0's
+    // device-scope acquire, a workgroup barrier, then the loads (the usual
+    // last-block pattern).  The partials are device-scope atomic stores and
+    // loads (sc1: written through and read past the XCD's L2), so the
+    // release's L2 write-back has little to flush.  Only thread 0 fences: the
+    // same fences in every wave (an L2 write-back each, and an invalidate of
+    // the L2 the other workgroups stream their K/V tiles through) slowed the
+    // split launch by up to 40%.
     if constexpr (XS) {
         constexpr int NX = RB * DB * 16 + 2 * RB;  // floats per lane
         constexpr int MO = RB * DB * 16;          // m_run at MO + rb, l_run at MO + RB + rb
@@ -811,19 +812,21 @@ void attn_fwd(AttnArgs a)
                 store_dev(&mine[(MO + RB + rb) * 64], l_run[rb]);
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // waits for the partial's stores
-        __syncthreads();  // every wave's stores are complete (and its LDS reads done)
+        __syncthreads();  // every wave's stores precede thread 0's release (and its LDS reads are done)
         typedef __attribute__((address_space(3))) int lds_i32;
         lds_i32 *const flag = (lds_i32 *)lds_all;
         if (threadIdx.x == 0) {
-            const unsigned seen = atomicAdd(a.ws_cnt + tile, 1u);
+            const unsigned seen = __hip_atomic_fetch_add(a.ws_cnt + tile, 1u, __ATOMIC_RELEASE,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
             const int last = seen == (unsigned)(a.n_split - 1);
-            if (last) atomicExch(a.ws_cnt + tile, 0u);
+            if (last) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every part's release is seen
+                atomicExch(a.ws_cnt + tile, 0u);
+            }
             *flag = last;
         }
-        __syncthreads();
+        __syncthreads();  // the other waves' loads follow thread 0's acquire
         if (!*flag) return;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // partial loads stay after the count
         // Merge in split order with a running max: part 0 is taken as is, and
         // part i rescales the sum so far by 2^(M - M') and adds its own by
         // 2^(m_i - M').  The order is fixed, so the result does not depend on
