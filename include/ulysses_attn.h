@@ -208,8 +208,10 @@ int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int ra
  */
 int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, void *stream);
 
-/* Work units (workgroups) of the attention launch for this shape; 0 for an
- * invalid or empty shape. */
+/* Work units (workgroups) of the attention launch of the calls without a
+ * workspace, and of attn_ulysses_fused_trace (its trace buffer holds 4 uint64
+ * per unit); 0 for an invalid or empty shape.  A *_ws call that splits runs
+ * ua_key_split workgroups per query tile of its own launch shape. */
 int64_t ua_work_units(const ua_shape *shp, int P);
 
 /* Static English text for a status code; never NULL. */
