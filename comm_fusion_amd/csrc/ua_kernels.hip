@@ -785,10 +785,10 @@ void attn_fwd(AttnArgs a)
     // the arrival, and let only the last arrival go on.  It merges the
     // partials of splits 0 .. n_split-1 in that order, resets the count for
     // the next call, and stores the rows.
-    // Ordering: the waves' partial stores, a workgroup barrier, then thread
-    // 0's device-scope release add; in the merging workgroup, thread 0's
-    // device-scope acquire, a workgroup barrier, then the loads (the usual
-    // last-block pattern).  The partials are device-scope atomic stores and
+    // Ordering: the waves' partial stores, each wave's wait for their
+    // completion, a workgroup barrier, then thread 0's device-scope release
+    // add; in the merging workgroup, thread 0's device-scope acquire, a
+    // workgroup barrier, then the loads (the usual last-block pattern).  The partials are device-scope atomic stores and
     // loads (sc1: written through and read past the XCD's L2), so the
     // release's L2 write-back has little to flush.  Only thread 0 fences: the
     // same fences in every wave (an L2 write-back each, and an invalidate of
@@ -812,7 +812,13 @@ void attn_fwd(AttnArgs a)
                 store_dev(&mine[(MO + RB + rb) * 64], l_run[rb]);
             }
         }
-        __syncthreads();  // every wave's stores precede thread 0's release (and its LDS reads are done)
+        // Each wave waits until its own partial stores have completed at
+        // device scope (an sc1 store counts as done once written through its
+        // XCD's L2) before the barrier; the barrier then orders every wave's
+        // completed stores before thread 0's release add.  The release's own
+        // wait covers only the stores of thread 0's wave.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // (also: every wave's LDS reads are done)
         typedef __attribute__((address_space(3))) int lds_i32;
         lds_i32 *const flag = (lds_i32 *)lds_all;
         if (threadIdx.x == 0) {

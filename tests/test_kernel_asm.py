@@ -193,3 +193,98 @@ def test_early_use_checker_catches_a_spill_before_the_wait():
     # a wait that leaves the read outstanding does not cover it
     late = ["ds_read_b128 v[96:99], v32", "s_waitcnt lgkmcnt(1)", "v_mov_b32_e32 v5, v97"]
     assert early_uses(late) == [(2, late[2])]
+
+
+# ---- key split: the partial stores are complete before the arrival count ----
+#
+# In a key-split build every storing wave writes its partial result with
+# device-scope (sc1) stores; a workgroup barrier follows, then one thread's
+# release add counts the arrival.  The release's own wait only covers the
+# stores of that thread's wave, so every wave must wait for its own stores
+# (s_waitcnt vmcnt(0)) before it reaches the barrier.
+
+_VM = re.compile(r"vmcnt\((\d+)\)")
+
+
+def _is_sc1_store(line: str) -> bool:
+    op = line.split(None, 1)[0]
+    return op.startswith(("global_store", "buffer_store", "flat_store")) and re.search(r"\bsc1\b", line) is not None
+
+
+def _store_step(pending: bool, line: str, bad, i):
+    op = line.split(None, 1)[0]
+    if op.startswith("s_waitcnt"):
+        m = _VM.search(line)
+        if m and int(m.group(1)) == 0:
+            return False
+        return pending
+    if op == "s_barrier" and pending and bad is not None:
+        bad.append((i, line))
+    if _is_sc1_store(line):
+        return True
+    return pending
+
+
+def barriers_with_stores_in_flight(lines):
+    """s_barrier instructions reachable while an sc1 store may be outstanding,
+    propagated over the control-flow graph (either path's stores count)."""
+    blocks, succ = _blocks(lines)
+    inn = [None] * len(blocks)
+    inn[0] = False
+    work = [0]
+    while work:
+        k = work.pop()
+        st = inn[k]
+        for i, line in blocks[k]:
+            st = _store_step(st, line, None, i)
+        for t in succ[k]:
+            m = st if inn[t] is None else (inn[t] or st)
+            if m != inn[t]:
+                inn[t] = m
+                work.append(t)
+    bad = []
+    for k, blk in enumerate(blocks):
+        st = bool(inn[k])
+        for i, line in blk:
+            st = _store_step(st, line, bad, i)
+    return bad
+
+
+def _split_kernels(asm):
+    # template argument XS is the first bool: ...Lb1ELb0E (XS = true, TRACE = false)
+    return {n: l for n, l in _kernel_bodies(asm).items() if "Lb1ELb0E" in n}
+
+
+def test_split_partials_complete_before_the_barrier(asm):
+    kernels = _split_kernels(asm)
+    assert len(kernels) >= 4, sorted(kernels)
+    for name, lines in kernels.items():
+        stores = [i for i, l in enumerate(lines) if _is_sc1_store(l)]
+        adds = [i for i, l in enumerate(lines) if l.startswith("global_atomic_add")]
+        assert stores and adds, name
+        # the check is not vacuous: a barrier lies between the partial stores and the add
+        assert any(l == "s_barrier" for l in lines[stores[-1]:adds[0]]), name
+        bad = barriers_with_stores_in_flight(lines)
+        assert not bad, "%s: %s" % (name, bad[:3])
+
+
+def test_store_checker_catches_a_barrier_before_the_wait():
+    # the ordering this check guards: partial stores, then a barrier whose
+    # preceding wait leaves them outstanding, then the release add
+    bad = ["global_store_dword v[66:67], v2, off sc1",
+           "s_waitcnt vmcnt(63) expcnt(7) lgkmcnt(15)",
+           "s_barrier",
+           "buffer_wbl2 sc1",
+           "s_waitcnt vmcnt(0)",
+           "global_atomic_add v1, v1, v66, s[2:3] sc0"]
+    assert barriers_with_stores_in_flight(bad) == [(2, "s_barrier")]
+    good = bad[:1] + ["s_waitcnt vmcnt(0)"] + bad[1:]
+    assert barriers_with_stores_in_flight(good) == []
+    # a store on one arm of a branch still counts at the join
+    branch = ["s_cbranch_execz .LBB0_2",
+              "global_store_dword v[66:67], v2, off sc1",
+              ".LBB0_2:",
+              "s_barrier"]
+    assert barriers_with_stores_in_flight(branch) == [(3, "s_barrier")]
+    # plain (non-sc1) stores, such as the epilogue's, are not partials
+    assert barriers_with_stores_in_flight(["global_store_dwordx2 v[0:1], v[2:3], off", "s_barrier"]) == []
