@@ -1,7 +1,7 @@
 """Benchmark: fused Ulysses-shard attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--seq-len S]
-                    [--no-cpu] [--no-split] [--no-io] [--cpu-seconds T] [--rounds R]
+                    [--no-cpu] [--no-split] [--no-io] [--no-long] [--cpu-seconds T] [--rounds R]
                     [--cpu-all] [--full-limit T] [--calibrate-copy MIB]
 
 One step = one attn_ulysses_fused call over the whole workload (attention over
@@ -11,7 +11,11 @@ with a workspace instead (attn_ulysses_fused_ws / attn_serial_ws: each query
 tile's keys split over several workgroups); detail.unsplit then times the
 plain call beside them, and --no-split times the plain calls throughout.
 Inputs are seeded synthetic bf16 tensors already resident in HBM when timing
-starts.  Prints ONE JSON line:
+starts.  Every timing follows W counted warm-up launches and at least 200 ms
+of launches in all, and is bracketed by two traced calls that read the shader
+clock; a timing whose clock drifts, or whose per-launch times spread, by more
+than the pages' +-2% DVFS envelope (review page, Fig. 11 caption) is flagged.
+Prints ONE JSON line:
   value     attention TFLOP/s of the fused call, counting 4*S^2*d per
             (batch, local head) (QK^T + PV, non-causal);
   roofline  the fused attention kernel against the bf16 MFMA peak, from HIP
@@ -24,6 +28,9 @@ starts.  Prints ONE JSON line:
             clock the kernel ran at; with both exchanges (detail.io): the
             call that reads Q, K, V in place from the sequence-partitioned
             inputs vs three separate gathers + attention + permute;
+  detail.long_configs  the same figures (timed region, medians, TFLOP/s and
+            fraction of the bf16 peak, traced clock and DVFS flag) for each
+            long-sequence workload: video_dit, dit_long and mixed;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -65,6 +72,8 @@ def parse():
                     help="time the calls without a workspace even where a key split would run")
     ap.add_argument("--no-io", action="store_true",
                     help="skip the timings with the pre-attention exchange (detail.io)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the other long-sequence workloads (detail.long_configs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--rounds", type=int, default=5,
@@ -278,6 +287,168 @@ def traced_call(ua, torch, q, k, v, w, dest) -> dict:
     }
 
 
+LONG_CONFIGS = ("video_dit", "dit_long", "mixed")   # the long-sequence workloads the target covers
+WARM_MS = 200.0          # launches run for at least this long before any timing
+DVFS_BAND = 0.02         # the pages' +-2% clock envelope (Fig. 11 caption)
+
+
+def warm_up(fn, count, min_ms):
+    """count launches, then further batches until at least min_ms of wall
+    time has passed since the first, so that timing starts at the clock the
+    GPU holds under this load rather than during its ramp."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(count):
+        fn()
+    torch.cuda.synchronize()
+    batch = 1
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        t1 = time.perf_counter()
+        for _ in range(batch):
+            fn()
+        torch.cuda.synchronize()
+        per = (time.perf_counter() - t1) * 1e3 / batch
+        batch = max(1, min(1000, int(20.0 / max(per, 1e-3))))
+
+
+def clock_flags(sclk_before, sclk_after, per_launch):
+    """DVFS check of one timing: the traced shader clock before and after it,
+    and the spread of the per-launch times (half the p10-p90 range over the
+    median); flagged when either leaves the +-2% band."""
+    mean = 0.5 * (sclk_before + sclk_after)
+    drift = (sclk_after - sclk_before) / mean if mean > 0 else None
+    med = float(np.median(per_launch))
+    spread = 0.5 * (np.percentile(per_launch, 90) - np.percentile(per_launch, 10)) / med
+    flag = (drift is None) or abs(drift) > DVFS_BAND or spread > DVFS_BAND
+    return {"sclk_mhz_before": round(sclk_before, 1), "sclk_mhz_after": round(sclk_after, 1),
+            "sclk_drift_pct": round(100 * drift, 2) if drift is not None else None,
+            "launch_spread_pct": round(100 * float(spread), 2),
+            "outside_dvfs_band": bool(flag)}
+
+
+class Case:
+    """One workload on the GPU: inputs resident in HBM, the destination
+    prefilled with the sentinel, and the callables that are timed."""
+
+    def __init__(self, ua, torch, w, dev, use_split=True, with_io=True):
+        from ua_inputs import SENTINEL_BITS, workload_qkv
+        self.w = w
+        self.ua = ua
+        self.torch = torch
+        Q, K, V = workload_qkv(w)
+        self.host = (Q, K, V)
+
+        def up(a):
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        q, k, v = up(Q), up(K), up(V)
+        self.q, self.k, self.v = q, k, v
+        n_dest = w.B * w.S * w.H * w.d
+        dest = torch.full((n_dest,), SENTINEL_BITS, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        o_local = torch.empty_like(q)
+        self.scratch_dest = torch.empty_like(dest)
+        self.n_split = ua.key_split(w.B, w.S, w.H, w.d, w.P) if use_split else 1
+        plain = lambda: ua.attn_ulysses_fused(q, k, v, w.rank, w.P, dest)  # noqa: E731
+        if self.n_split > 1:
+            ws = ua.new_workspace(w.B, w.S, w.H, w.d, w.P, dev)
+            self.ws = ws
+            fused = lambda: ua.attn_ulysses_fused_ws(q, k, v, w.rank, w.P, dest, ws)  # noqa: E731
+            alone = lambda: ua.attn_serial_ws(q, k, v, w.rank, w.P, o_local, ws)      # noqa: E731
+        else:
+            fused = plain
+            alone = lambda: ua.attn_serial(q, k, v, w.rank, w.P, o_local)  # noqa: E731
+        perm = lambda: ua.a2a_permute(o_local, w.rank, w.P, dest)           # noqa: E731
+        sd = self.scratch_dest
+        store_only = lambda: ua.epilogue_store_only(w.B, w.S, w.H, w.d, w.rank, w.P, sd)  # noqa: E731
+
+        def serial():
+            alone()
+            perm()
+
+        self.fused = fused
+        self.fns = {"fused": fused, "serial": serial, "alone": alone, "perm": perm, "store_only": store_only}
+        if self.n_split > 1:
+            self.fns["unsplit"] = plain
+        if with_io:
+            # Sequence-partitioned inputs [B][P][S/P][H][d] holding the rank's
+            # Q, K, V in its head slots (the other heads are never read).
+            lo, hi = w.rank * w.Hl, (w.rank + 1) * w.Hl
+            xs = []
+            for t in (q, k, v):
+                X = torch.zeros((w.B, w.S, w.H, w.d), dtype=torch.bfloat16, device=dev)
+                X[:, :, lo:hi] = t.view(w.B, w.S, w.Hl, w.d)
+                xs.append(X)
+            g_loc = [torch.empty_like(q) for _ in range(3)]
+            if self.n_split > 1:
+                self.fns["fused_io"] = lambda: ua.attn_ulysses_fused_io_ws(xs[0], xs[1], xs[2], w.rank, w.P, dest, ws)
+            else:
+                self.fns["fused_io"] = lambda: ua.attn_ulysses_fused_io(xs[0], xs[1], xs[2], w.rank, w.P, dest)
+            self.fns["gather"] = lambda: ua.a2a_gather(xs[0], w.rank, w.P, g_loc[0])
+
+            def serial_io():
+                for X, L in zip(xs, g_loc):
+                    ua.a2a_gather(X, w.rank, w.P, L)
+                if self.n_split > 1:
+                    ua.attn_serial_ws(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local, ws)
+                else:
+                    ua.attn_serial(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local)
+                perm()
+            self.fns["serial_io"] = serial_io
+        torch.cuda.synchronize()
+
+    def traced(self):
+        return traced_call(self.ua, self.torch, self.q, self.k, self.v, self.w, self.scratch_dest)
+
+    def measure(self, steps, warmup, rounds):
+        """Warm-up (counted and timed), the traced clock, K fused launches back
+        to back (the timed region), interleaved rounds of every callable, and
+        the traced clock again."""
+        w = self.w
+        warm_up(self.fused, warmup, WARM_MS)
+        before = self.traced()
+        per, total_ms, wall_ms = time_launches(self.fused, steps, 0)
+        # about 100 ms of each callable per round (at most 500 launches)
+        reps = max(2, min(500, int(100.0 / max(float(np.mean(per)), 1e-3)) + 1))
+        cmp = interleaved(self.fns, rounds, reps)
+        after = self.traced()
+        med = lambda x: float(np.median(x))  # noqa: E731
+        t_f, t_s, t_a = med(cmp["fused"]), med(cmp["serial"]), med(cmp["alone"])
+        ms_step = total_ms / steps
+        r = {
+            "per": per, "total_ms": total_ms, "wall_ms": wall_ms, "cmp": cmp, "before": before, "after": after,
+            "ms_step": ms_step,
+            "value": w.flops / (ms_step * 1e-3) / 1e12,
+            "launch_ms": float(np.mean(per)),
+            "t_f": t_f, "t_s": t_s, "t_a": t_a, "t_p": med(cmp["perm"]),
+        }
+        r["clock"] = clock_flags(before["sclk_mhz_trace"], after["sclk_mhz_trace"], per)
+        return r
+
+    def summary(self, r):
+        """The per-workload entry of detail.long_configs."""
+        w = self.w
+        tf = lambda t: round(w.flops / (t * 1e-3) / 1e12, 2)  # noqa: E731
+        out = {
+            "workload": w.name, "B": w.B, "S": w.S, "Hl": w.Hl, "d": w.d, "flops": w.flops,
+            "key_split": self.n_split,
+            "timed_region_ms_per_step": round(r["ms_step"], 4),
+            "timed_region_TFLOPs": round(r["value"], 2),
+            "frac": round(r["value"] / PEAK_BF16_TFLOPS, 4),
+            "fused_ms_median": round(r["t_f"], 4),
+            "fused_TFLOPs_median": tf(r["t_f"]),
+            "frac_median": round(w.flops / (r["t_f"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "serial_ms_median": round(r["t_s"], 4),
+            "attn_alone_ms_median": round(r["t_a"], 4),
+            "permute_ms_median": round(r["t_p"], 4),
+            "residual_fused_vs_alone": round((r["t_f"] - r["t_a"]) / r["t_a"], 4),
+            "speedup_serial_over_fused": round(r["t_s"] / r["t_f"], 4),
+            **r["clock"],
+        }
+        if "unsplit" in r["cmp"]:
+            out["unsplit_fused_ms_median"] = round(float(np.median(r["cmp"]["unsplit"])), 4)
+        return out
+
+
 def main():
     args = parse()
     if args.cpu_all:
@@ -291,7 +462,7 @@ def main():
     import torch
 
     import comm_fusion_amd as ua
-    from ua_inputs import SENTINEL_BITS, WORKLOADS, workload_qkv
+    from ua_inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
     if args.seq_len:
@@ -299,63 +470,8 @@ def main():
             sys.exit("--seq-len must be a multiple of P = %d" % w.P)
         w = dataclasses.replace(w, name="%s_S%d" % (w.name, args.seq_len), S=args.seq_len, sampled=True)
         args.no_cpu = True
+        args.no_long = True
     dev = torch.device("cuda:0")
-    Q, K, V = workload_qkv(w)
-
-    def up(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-
-    q, k, v = up(Q), up(K), up(V)
-    n_dest = w.B * w.S * w.H * w.d
-    dest = torch.full((n_dest,), SENTINEL_BITS, dtype=torch.int16, device=dev).view(torch.bfloat16)
-    o_local = torch.empty_like(q)
-    torch.cuda.synchronize()
-
-    n_split = 1 if args.no_split else ua.key_split(w.B, w.S, w.H, w.d, w.P)
-    plain = lambda: ua.attn_ulysses_fused(q, k, v, w.rank, w.P, dest)  # noqa: E731
-    if n_split > 1:
-        ws = ua.new_workspace(w.B, w.S, w.H, w.d, w.P, dev)
-        fused = lambda: ua.attn_ulysses_fused_ws(q, k, v, w.rank, w.P, dest, ws)  # noqa: E731
-        alone = lambda: ua.attn_serial_ws(q, k, v, w.rank, w.P, o_local, ws)      # noqa: E731
-    else:
-        fused = plain
-        alone = lambda: ua.attn_serial(q, k, v, w.rank, w.P, o_local)  # noqa: E731
-    perm = lambda: ua.a2a_permute(o_local, w.rank, w.P, dest)           # noqa: E731
-    scratch_dest = torch.empty_like(dest)
-    store_only = lambda: ua.epilogue_store_only(w.B, w.S, w.H, w.d, w.rank, w.P, scratch_dest)  # noqa: E731
-
-    def serial():
-        alone()
-        perm()
-
-    fns = {"fused": fused, "serial": serial, "alone": alone, "perm": perm, "store_only": store_only}
-    if n_split > 1:
-        fns["unsplit"] = plain
-    if not args.no_io:
-        # Sequence-partitioned inputs [B][P][S/P][H][d] holding the rank's
-        # Q, K, V in its head slots (the other heads are never read).
-        lo, hi = w.rank * w.Hl, (w.rank + 1) * w.Hl
-        xs = []
-        for t in (q, k, v):
-            X = torch.zeros((w.B, w.S, w.H, w.d), dtype=torch.bfloat16, device=dev)
-            X[:, :, lo:hi] = t.view(w.B, w.S, w.Hl, w.d)
-            xs.append(X)
-        g_loc = [torch.empty_like(q) for _ in range(3)]
-        if n_split > 1:
-            fns["fused_io"] = lambda: ua.attn_ulysses_fused_io_ws(xs[0], xs[1], xs[2], w.rank, w.P, dest, ws)
-        else:
-            fns["fused_io"] = lambda: ua.attn_ulysses_fused_io(xs[0], xs[1], xs[2], w.rank, w.P, dest)
-        fns["gather"] = lambda: ua.a2a_gather(xs[0], w.rank, w.P, g_loc[0])
-
-        def serial_io():
-            for X, L in zip(xs, g_loc):
-                ua.a2a_gather(X, w.rank, w.P, L)
-            if n_split > 1:
-                ua.attn_serial_ws(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local, ws)
-            else:
-                ua.attn_serial(g_loc[0], g_loc[1], g_loc[2], w.rank, w.P, o_local)
-            perm()
-        fns["serial_io"] = serial_io
 
     if args.calibrate_copy:
         src = torch.empty(args.calibrate_copy << 20, dtype=torch.uint8, device=dev)
@@ -365,21 +481,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # The timed region: K fused steps back to back.
-    per, total_ms, wall_ms = time_launches(fused, args.steps, args.warmup)
-    # Baselines: fused, serial (attention + separate permute), attention
-    # alone and permute alone, in interleaved rounds.
-    reps = max(2, min(args.steps, int(200.0 / max(float(np.mean(per)), 1e-3)) + 1))
-    cmp = interleaved(fns, args.rounds, reps)
-    per_serial, per_alone, per_perm = cmp["serial"], cmp["alone"], cmp["perm"]
-    tr = traced_call(ua, torch, q, k, v, w, scratch_dest)
-
-    ms_step = total_ms / args.steps
-    value = w.flops / (ms_step * 1e-3) / 1e12
-    launch_ms = float(np.mean(per))
+    case = Case(ua, torch, w, dev, use_split=not args.no_split, with_io=not args.no_io)
+    n_split = case.n_split
+    # The timed region: K fused steps back to back, after the warm-up; then
+    # fused, serial (attention + separate permute), attention alone and
+    # permute alone in interleaved rounds.
+    r = case.measure(args.steps, args.warmup, args.rounds)
+    per, cmp, tr = r["per"], r["cmp"], r["after"]
+    ms_step, value, launch_ms = r["ms_step"], r["value"], r["launch_ms"]
     achieved = w.flops / (launch_ms * 1e-3) / 1e12
     med = lambda x: float(np.median(x))  # noqa: E731
-    t_f, t_s, t_a, t_p = med(cmp["fused"]), med(per_serial), med(per_alone), med(per_perm)
+    t_f, t_s, t_a, t_p = r["t_f"], r["t_s"], r["t_a"], r["t_p"]
     traffic = measured_traffic(w.name) if n_split == 1 else None
     unsplit = None
     if n_split > 1:
@@ -399,6 +511,25 @@ def main():
               "speedup_serial_io_over_fused_io": round(t_sio / t_fio, 4),
               "residual_fused_io_vs_alone": round((t_fio - t_a) / t_a, 4),
               "fused_io_TFLOPs": round(w.flops / (t_fio * 1e-3) / 1e12, 2)}
+
+    # The other long-sequence workloads, measured the same way (one entry
+    # each; the headline workload's entry repeats its own figures).
+    long_configs = None
+    if not args.no_long:
+        long_configs = {w.name: case.summary(r)} if w.name in LONG_CONFIGS else {}
+        host = case.host
+        del case
+        torch.cuda.empty_cache()
+        for name in LONG_CONFIGS:
+            if name in long_configs:
+                continue
+            c = Case(ua, torch, WORKLOADS[name], dev, use_split=not args.no_split, with_io=False)
+            long_configs[name] = c.summary(c.measure(args.steps, args.warmup, args.rounds))
+            print(json.dumps({"long_config": long_configs[name]}), file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+    else:
+        host = case.host
 
     out = {
         "metric": METRIC,
@@ -421,6 +552,7 @@ def main():
                      "traffic": traffic},
         "detail": {
             "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+            "warmup_ms_min": WARM_MS,
             "fused_ms_median": round(t_f, 4), "fused_ms_min": round(min(cmp["fused"]), 4),
             "timed_region_launch_ms_mean": round(launch_ms, 4),
             "serial_ms_median": round(t_s, 4),
@@ -434,16 +566,19 @@ def main():
             "store_only_epilogue_ms_median": round(med(cmp["store_only"]), 4),
             "store_only_epilogue_GBs": round(w.out_bytes / (med(cmp["store_only"]) * 1e-3) / 1e9, 1),
             **tr,
+            "clock": r["clock"],
             # the same against the peak scaled to the clock the traced call ran at
             "pct_bf16_peak_at_traced_clock": round(100.0 * value / (PEAK_BF16_TFLOPS * tr["sclk_mhz_trace"] / 2400.0), 2)
             if tr.get("sclk_mhz_trace") and n_split == 1 else None,
             "split": unsplit,
             "io": io,
-            "wall_ms_timed_region": round(wall_ms, 3),
+            "long_configs": long_configs,
+            "wall_ms_timed_region": round(r["wall_ms"], 3),
             "kernel_code_sha256_16": source_digest(),
         },
     }
     if not args.no_cpu:
+        Q, K, V = host
         out["cpu_baseline"] = cpu_baseline(w, Q, K, V, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

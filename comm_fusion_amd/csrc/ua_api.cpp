@@ -94,7 +94,7 @@ ua::Placement local_placement(void *o_local, const ua_shape *shp, int P)
 // want_ws: a *_ws call, whose workspace (ws_bytes bytes) lets the launch
 // split the keys of each query tile over several workgroups.
 int attention_call(const void *Q, const void *K, const void *V, int rank, int P, void *out,
-                   const ua_shape *shp, float scale, void *stream, bool fused, uint64_t *trace = nullptr,
+                   const ua_shape *shp, float scale, hipStream_t stream, bool fused, uint64_t *trace = nullptr,
                    bool want_trace = false, bool seq_input = false, bool want_ws = false,
                    void *ws = nullptr, size_t ws_bytes = 0)
 {
@@ -130,20 +130,20 @@ int attention_call(const void *Q, const void *K, const void *V, int rank, int P,
 extern "C" {
 
 int attn_ulysses_fused(const void *Q, const void *K, const void *V, int rank, int P, void *out,
-                       const ua_shape *shp, float scale, void *stream)
+                       const ua_shape *shp, float scale, hipStream_t stream)
 {
     return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true);
 }
 
 int attn_serial(const void *Q, const void *K, const void *V, int rank, int P, void *O_local,
-                const ua_shape *shp, float scale, void *stream)
+                const ua_shape *shp, float scale, hipStream_t stream)
 {
     return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false);
 }
 
 int attn_ulysses_fused_ws(const void *Q, const void *K, const void *V, int rank, int P, void *out,
                           const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
-                          void *stream)
+                          hipStream_t stream)
 {
     return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, nullptr, false, false, true,
                           workspace, workspace_bytes);
@@ -151,7 +151,7 @@ int attn_ulysses_fused_ws(const void *Q, const void *K, const void *V, int rank,
 
 int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P, void *O_local,
                    const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
-                   void *stream)
+                   hipStream_t stream)
 {
     return attention_call(Q, K, V, rank, P, O_local, shp, scale, stream, false, nullptr, false, false, true,
                           workspace, workspace_bytes);
@@ -159,7 +159,7 @@ int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
 
 int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int rank, int P, void *out,
                              const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
-                             void *stream)
+                             hipStream_t stream)
 {
     return attention_call(Xq, Xk, Xv, rank, P, out, shp, scale, stream, true, nullptr, false, true, true,
                           workspace, workspace_bytes);
@@ -190,12 +190,12 @@ int ua_key_split(const ua_shape *shp, int P)
 }
 
 int attn_ulysses_fused_io(const void *Xq, const void *Xk, const void *Xv, int rank, int P, void *out,
-                          const ua_shape *shp, float scale, void *stream)
+                          const ua_shape *shp, float scale, hipStream_t stream)
 {
     return attention_call(Xq, Xk, Xv, rank, P, out, shp, scale, stream, true, nullptr, false, true);
 }
 
-int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *shp, void *stream)
+int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *shp, hipStream_t stream)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);
@@ -212,12 +212,12 @@ int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *sh
 }
 
 int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int rank, int P, void *out,
-                             const ua_shape *shp, float scale, void *stream, uint64_t *trace)
+                             const ua_shape *shp, float scale, hipStream_t stream, uint64_t *trace)
 {
     return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, trace, true);
 }
 
-int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, void *stream)
+int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, hipStream_t stream)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);
@@ -239,7 +239,7 @@ int64_t ua_work_units(const ua_shape *shp, int P)
     return ua::attention_units(shp->B, shp->S, shp->H / P, (int)shp->d);
 }
 
-int a2a_permute(const void *O_local, int rank, int P, void *out, const ua_shape *shp, void *stream)
+int a2a_permute(const void *O_local, int rank, int P, void *out, const ua_shape *shp, hipStream_t stream)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);

@@ -58,6 +58,7 @@
 
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -91,6 +92,7 @@ struct AttnArgs {
     int32_t in_head0;  // this rank's first head among them (0, or rank*Hl)
     int32_t n_qtiles;
     int32_t n_units;
+    int32_t n_xcd;     // XCDs of the device (workgroups are dealt round robin over them)
     float scale_log2;  // softmax scale * log2(e)
     uint64_t *trace;   // measurement build only: 4 timestamps per work unit
     // key split across workgroups (XS builds only): n_split workgroups per
@@ -181,13 +183,14 @@ __device__ __forceinline__ void static_for(F &&f)
     static_for_impl(std::make_integer_sequence<int, N>(), f);
 }
 
-// Logical work unit of this workgroup.  Workgroup i is dispatched to XCD
-// i % 8; give each XCD a contiguous run of units (same head, neighbouring Q
-// tiles) so they share K/V in that XCD's L2.  A bijection on [0, n).
-__device__ __forceinline__ int xcd_unit(int bid, int n)
+// Logical work unit of this workgroup.  Workgroups are dispatched round
+// robin over the device's nx XCDs (workgroup i to XCD i % nx); give each XCD
+// a contiguous run of units (same head, neighbouring Q tiles) so they share
+// K/V in that XCD's L2.  A bijection on [0, n).
+__device__ __forceinline__ int xcd_unit(int bid, int n, int nx)
 {
-    const int xcd = bid & 7, k = bid >> 3;
-    const int q = n >> 3, r = n & 7;
+    const int xcd = bid % nx, k = bid / nx;
+    const int q = n / nx, r = n % nx;
     return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
 }
 
@@ -263,7 +266,7 @@ void attn_fwd(AttnArgs a)
 
     // Unit u = ((b*Hl + h)*n_split + split)*n_qtiles + qt: the units that run
     // side by side on one XCD read the same keys.
-    const int unit = xcd_unit(blockIdx.x, a.n_units);
+    const int unit = xcd_unit(blockIdx.x, a.n_units, a.n_xcd);
     const int qt = unit % a.n_qtiles;
     const int split = XS ? unit / a.n_qtiles % a.n_split : 0;
     const int bh = XS ? unit / a.n_qtiles / a.n_split : unit / a.n_qtiles;
@@ -937,12 +940,12 @@ void attn_fwd(AttnArgs a)
 // positive).  Measures what the destination layout sustains.
 template <int D, int NW, int RB, int KS>
 __global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S, int32_t Hl, int32_t n_qtiles,
-                                                         int32_t n_units)
+                                                         int32_t n_units, int32_t n_xcd)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int il = lane & 31, g = lane >> 5;
-    const int unit = xcd_unit(blockIdx.x, n_units);
+    const int unit = xcd_unit(blockIdx.x, n_units, n_xcd);
     const int qt = unit % n_qtiles;
     const int bh = unit / n_qtiles;
     const int h = bh % Hl;
@@ -1010,29 +1013,62 @@ __global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chun
     *(u32x4 *)(dst + (int64_t)c * 8) = *(const u32x4 *)src;
 }
 
+// Compute units and XCDs of the current device, queried once per device.
+// Without a device (the size queries run on hosts without a GPU) the full
+// MI355X is assumed: 256 CUs in 8 XCDs.  A failed query leaves no error
+// behind for the caller's next hipGetLastError.
+struct DeviceInfo {
+    int cus, xcds;
+};
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_cus[kMaxDevices];
+std::atomic<int> g_dev_xcds[kMaxDevices];
+
+DeviceInfo device_info()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return {256, 8};
+    }
+    int cus = g_dev_cus[dev].load(std::memory_order_relaxed);
+    int xcds = g_dev_xcds[dev].load(std::memory_order_relaxed);
+    if (cus > 0 && xcds > 0) return {cus, xcds};
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcds <= 0) {
+        (void)hipGetLastError();
+        xcds = 1;
+    }
+    g_dev_cus[dev].store(cus, std::memory_order_relaxed);
+    g_dev_xcds[dev].store(xcds, std::memory_order_relaxed);
+    return {cus, xcds};
+}
+
 // Launch shape of the attention kernel for a problem: waves per workgroup,
-// 32-row blocks per wave, keys per K/V tile, key groups.  With at least 128
-// units of 256 rows (half a workgroup per CU): 8 waves on 64-key tiles (one
-// K/V tile per 256 query rows); for d = 64, 8 waves of two row blocks each
-// on 32-key tiles (512 rows per unit; each LDS operand fragment feeds two
-// MFMAs, ~4% faster per row) when that also gives at least 128 units and its
-// estimated time -- rounds of units over the MI355X's 256 CUs times the rows
-// a unit processes -- is at most 25/24 of the other's.  Below 128 units:
-// 128-row units, as two key groups of 4 waves on 32-key tiles when the
-// 32-key tile count is even, else as 4 waves on 64-key tiles.
+// 32-row blocks per wave, keys per K/V tile, key groups.  With at least
+// cus/2 units of 256 rows (half a workgroup per CU; 128 on the MI355X's 256
+// CUs): 8 waves on 64-key tiles (one K/V tile per 256 query rows); for
+// d = 64, 8 waves of two row blocks each on 32-key tiles (512 rows per unit;
+// each LDS operand fragment feeds two MFMAs, ~4% faster per row) when that
+// also gives at least cus/2 units and its estimated time -- rounds of units
+// over the CUs times the rows a unit processes -- is at most 25/24 of the
+// other's.  Below cus/2 units: 128-row units, as two key groups of 4 waves
+// on 32-key tiles when the 32-key tile count is even, else as 4 waves on
+// 64-key tiles.
 struct LaunchShape {
     int nw, rb, kb, ks;
     int rows() const { return 32 * rb * nw / ks; }
 };
 
-constexpr int64_t kCUs = 256;
-
-LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
+LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d, int64_t cus)
 {
     const auto units = [&](int64_t rows) { return B * Hl * ((S + rows - 1) / rows); };
     // rounds of units over the CUs times the rows a unit processes
-    const auto cost = [&](int64_t rows) { return (units(rows) + kCUs - 1) / kCUs * (S < rows ? S : rows); };
-    if (units(256) < 128) {
+    const auto cost = [&](int64_t rows) { return (units(rows) + cus - 1) / cus * (S < rows ? S : rows); };
+    if (units(256) < cus / 2) {
         // 128-row units: two key groups of 4 waves on 32-key tiles (two waves
         // per SIMD) when the tile count is even, else 4 waves (one per SIMD)
         const int64_t nt = (S + 31) / 32;
@@ -1040,18 +1076,18 @@ LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d)
         return {4, 1, 64, 1};
     }
     // per-row time of the two-row-block shape: 24/25 of the one-row-block one
-    if (d == 64 && units(512) >= 128 && cost(512) * 24 <= cost(256) * 25) return {8, 2, 32, 1};
+    if (d == 64 && units(512) >= cus / 2 && cost(512) * 24 <= cost(256) * 25) return {8, 2, 32, 1};
     return {8, 1, 64, 1};
 }
 
 // Key split across workgroups for launches with fewer than 1024 query tiles
 // (four rounds over the CUs), where too few tiles or a last round that fills
 // the CUs poorly leave CUs idle: the launch shape and the number n of
-// workgroups per query tile.  The
+// workgroups per query tile, for a device of `cus` compute units.  The
 // candidates are the plain call's shape and, where that shape uses 128-row
-// units (fewer than 128 units of 256 rows), the 256-row shape on 64-key
+// units (fewer than cus/2 units of 256 rows), the 256-row shape on 64-key
 // tiles; only 8-wave shapes split.  Each candidate with n in 1 .. 4 costs
-// (rounds of n * units over the 256 CUs) * (keys one wave processes + 512
+// (rounds of n * units over the CUs) * (keys one wave processes + 512
 // + 128 (n - 1)): 512 keys' worth of time stand for a workgroup's fixed cost
 // (prologue, partial write, count) and 128 for each part the merging
 // workgroup loads (one memory round trip), both fitted to measured 2- to
@@ -1071,14 +1107,14 @@ struct SplitPlan {
     int n;
 };
 
-SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d)
+SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d, int64_t cus)
 {
-    const LaunchShape plain = launch_shape(B, S, Hl, d);
+    const LaunchShape plain = launch_shape(B, S, Hl, d, cus);
     const auto units = [&](const LaunchShape &ls) { return B * Hl * ((S + ls.rows() - 1) / ls.rows()); };
     SplitPlan best = {plain, 1};
     if (units(plain) >= kSplitMaxTiles) return best;
     const int64_t U0 = (S + plain.kb - 1) / plain.kb / plain.ks;
-    int64_t best_cost = (units(plain) + kCUs - 1) / kCUs * (U0 * plain.kb + kSplitFixedKeys);
+    int64_t best_cost = (units(plain) + cus - 1) / cus * (U0 * plain.kb + kSplitFixedKeys);
     LaunchShape cands[2] = {plain, {8, 1, 64, 1}};
     const int ncand = plain.rows() == 128 ? 2 : 1;
     for (int n = 1; n <= kSplitMaxN; ++n)
@@ -1087,7 +1123,7 @@ SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d)
             if (ls.nw != 8 || (n == 1 && c > 0)) continue;
             const int64_t U = (S + ls.kb - 1) / ls.kb / ls.ks;  // units of ks tiles
             if (n > 1 && U / n < kMinSplitUnits) continue;
-            const int64_t cost = (units(ls) * n + kCUs - 1) / kCUs *
+            const int64_t cost = (units(ls) * n + cus - 1) / cus *
                                  ((U + n - 1) / n * ls.kb + kSplitFixedKeys + kSplitPartKeys * (n - 1));
             if (cost < best_cost) {
                 best = {ls, n};
@@ -1142,21 +1178,21 @@ int64_t part_floats_per_split(const LaunchShape &ls, int d)
 
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const LaunchShape ls = launch_shape(B, S, Hl, d);
+    const LaunchShape ls = launch_shape(B, S, Hl, d, device_info().cus);
     return B * Hl * ((S + ls.rows() - 1) / ls.rows());
 }
 
-int key_split(int64_t B, int64_t S, int64_t Hl, int d) { return split_plan(B, S, Hl, d).n; }
+int key_split(int64_t B, int64_t S, int64_t Hl, int d) { return split_plan(B, S, Hl, d, device_info().cus).n; }
 
 int64_t workspace_count_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const SplitPlan sp = split_plan(B, S, Hl, d);
+    const SplitPlan sp = split_plan(B, S, Hl, d, device_info().cus);
     return sp.n == 1 ? 0 : kCountBytes;
 }
 
 int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 {
-    const SplitPlan sp = split_plan(B, S, Hl, d);
+    const SplitPlan sp = split_plan(B, S, Hl, d, device_info().cus);
     if (sp.n == 1) return 0;
     const int64_t tiles = B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows());
     return kCountBytes + tiles * sp.n * part_floats_per_split(sp.ls, d) * 4;
@@ -1167,7 +1203,9 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             int d, float scale, const Placement &out, hipStream_t stream,
                             uint64_t *trace, void *workspace)
 {
-    const SplitPlan sp = workspace && !trace ? split_plan(B, S, Hl, d) : SplitPlan{launch_shape(B, S, Hl, d), 1};
+    const DeviceInfo dv = device_info();
+    const SplitPlan sp = workspace && !trace ? split_plan(B, S, Hl, d, dv.cus)
+                                             : SplitPlan{launch_shape(B, S, Hl, d, dv.cus), 1};
     const LaunchShape ls = sp.ls;
     const int n_split = sp.n;
     AttnArgs a;
@@ -1181,6 +1219,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.in_head0 = (int32_t)in_head0;
     a.n_qtiles = (int32_t)((S + ls.rows() - 1) / ls.rows());
     a.n_units = (int32_t)(B * Hl * a.n_qtiles);
+    a.n_xcd = dv.xcds;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.trace = trace;
     a.n_split = n_split;
@@ -1202,13 +1241,15 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,
                                 hipStream_t stream)
 {
-    const LaunchShape ls = launch_shape(B, S, Hl, d);
+    const DeviceInfo dv = device_info();
+    const LaunchShape ls = launch_shape(B, S, Hl, d, dv.cus);
     Placement o = out;
     int64_t S64 = S;
     int32_t Hl32 = (int32_t)Hl;
     int32_t n_qtiles = (int32_t)((S + ls.rows() - 1) / ls.rows());
-    int32_t n_units = (int32_t)attention_units(B, S, Hl, d);
-    void *args[] = {&o, &S64, &Hl32, &n_qtiles, &n_units};
+    int32_t n_units = (int32_t)(B * Hl * n_qtiles);
+    int32_t n_xcd = dv.xcds;
+    void *args[] = {&o, &S64, &Hl32, &n_qtiles, &n_units, &n_xcd};
     const void *fn;
     if (ls.ks == 2)
         fn = d == 128 ? (const void *)epilogue_only<128, 8, 1, 2> : (const void *)epilogue_only<64, 8, 1, 2>;

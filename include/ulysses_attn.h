@@ -43,7 +43,10 @@
  * Pointers Q, K, V, out, O_local are DEVICE pointers on the current HIP
  * device, 16-byte aligned.  `stream` is a hipStream_t of that device
  * (NULL = its default stream).  Calls are asynchronous: they return after
- * the launch.
+ * the launch.  Launch shapes (and so ua_work_units, ua_key_split and the
+ * workspace sizes) follow the current device's compute-unit and XCD counts,
+ * queried once per device; on a host without a device they are computed for
+ * the full MI355X (256 CUs in 8 XCDs).
  *
  * Errors: every call returns a status code and never prints or aborts.
  * Arguments are validated on the host before any device access, in this
@@ -61,6 +64,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -92,7 +97,7 @@ enum {
  * B == 0 or S == 0 is a valid empty call (no launch, UA_OK).
  */
 int attn_ulysses_fused(const void *Q, const void *K, const void *V, int rank, int P,
-                       void *out, const ua_shape *shp, float scale, void *stream);
+                       void *out, const ua_shape *shp, float scale, hipStream_t stream);
 
 /*
  * Serial baseline, attention half ("FlashAttention alone" in the abstract):
@@ -100,7 +105,7 @@ int attn_ulysses_fused(const void *Q, const void *K, const void *V, int rank, in
  * [B][S][Hl][d].  rank and P are validated like the fused call and fix Hl.
  */
 int attn_serial(const void *Q, const void *K, const void *V, int rank, int P,
-                void *O_local, const ua_shape *shp, float scale, void *stream);
+                void *O_local, const ua_shape *shp, float scale, hipStream_t stream);
 
 /*
  * Serial baseline, exchange half (the post-attention All-to-All of Fig. 5,
@@ -110,7 +115,7 @@ int attn_serial(const void *Q, const void *K, const void *V, int rank, int P,
  * attn_ulysses_fused writes.
  */
 int a2a_permute(const void *O_local, int rank, int P, void *out,
-                const ua_shape *shp, void *stream);
+                const ua_shape *shp, hipStream_t stream);
 
 /*
  * The fused and serial calls with a workspace, for shapes whose query tiles
@@ -140,16 +145,16 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
  */
 int attn_ulysses_fused_ws(const void *Q, const void *K, const void *V, int rank, int P,
                           void *out, const ua_shape *shp, float scale, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          size_t workspace_bytes, hipStream_t stream);
 int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
                    void *O_local, const ua_shape *shp, float scale, void *workspace,
-                   size_t workspace_bytes, void *stream);
+                   size_t workspace_bytes, hipStream_t stream);
 /* attn_ulysses_fused_io (below) with a workspace, as the two calls above:
  * bit-identical to a2a_gather of Xq, Xk, Xv followed by
  * attn_ulysses_fused_ws on the same workspace. */
 int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int rank, int P,
                              void *out, const ua_shape *shp, float scale, void *workspace,
-                             size_t workspace_bytes, void *stream);
+                             size_t workspace_bytes, hipStream_t stream);
 /* Workspace bytes the *_ws calls need for this shape (0: no split, or an
  * invalid or empty shape). */
 size_t ua_workspace_bytes(const ua_shape *shp, int P);
@@ -172,14 +177,14 @@ int ua_key_split(const ua_shape *shp, int P);
  * attn_ulysses_fused.  Validation as attn_ulysses_fused, plus H*d <= 2^24.
  */
 int attn_ulysses_fused_io(const void *Xq, const void *Xk, const void *Xv, int rank, int P,
-                          void *out, const ua_shape *shp, float scale, void *stream);
+                          void *out, const ua_shape *shp, float scale, hipStream_t stream);
 /*
  * Serial baseline of the pre-attention exchange (Fig. 5 steps a-c, run as a
  * separate step): copies this rank's Hl heads of every row of X
  * [B][P][S/P][H][d] bit-for-bit into X_local [B][S][Hl][d] (row s from
  * region s / (S/P), local row s mod (S/P)).  Validation as a2a_permute.
  */
-int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *shp, void *stream);
+int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *shp, hipStream_t stream);
 /*
  * Measurement build of attn_ulysses_fused (the per-tile store spans the
  * pages time for the piggybacked epilogue; review page, Fig. 7): the same
@@ -196,7 +201,7 @@ int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *sh
  * aligned, owned by the caller; NULL gives UA_ERR_NULL (for a non-empty call).
  */
 int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int rank, int P,
-                             void *out, const ua_shape *shp, float scale, void *stream,
+                             void *out, const ua_shape *shp, float scale, hipStream_t stream,
                              uint64_t *trace);
 
 /*
@@ -206,7 +211,7 @@ int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int ra
  * g, column c) of this rank's slots gets bf16 bits (7*s + 13*g + 3*c) & 0x3FFF;
  * every other slot keeps its bytes.  Validation as a2a_permute.
  */
-int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, void *stream);
+int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, hipStream_t stream);
 
 /* Work units (workgroups) of the attention launch of the calls without a
  * workspace, and of attn_ulysses_fused_trace (its trace buffer holds 4 uint64
