@@ -16,6 +16,8 @@ Names and arguments follow the C calls:
   attn_ulysses_fused_ws(Q, K, V, rank, P, out, workspace, scale=None, stream=None)
   attn_serial_ws(Q, K, V, rank, P, O_local, workspace, scale=None, stream=None)
   attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, out, workspace, scale=None, stream=None)
+  attn_ulysses_fused_noalloc(Q, K, V, rank, P, out, scale=None, stream=None)
+      (the _ws call with its workspace in the library's fixed device scratch)
   workspace_bytes(B, S, H, d, P), workspace_count_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
   new_workspace(B, S, H, d, P, device)  (a zeroed uint8 tensor, or None)
 and, for measurement only,
@@ -28,10 +30,11 @@ Tensors are torch tensors on the GPU: Q, K, V, O_local bfloat16
 [B][P][S/P][H][d] (or the same bytes viewed as [B][S][H][d]).
 """
 from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # noqa: F401
-                       UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_OK, UAError,
+                       UA_ERR_SCRATCH, UA_ERR_SHAPE, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_OK,
+                       SCRATCH_BYTES, UAError,
                        a2a_gather, a2a_permute, attn_serial, attn_serial_ws, attn_ulysses_fused,
                        attn_ulysses_fused_io, attn_ulysses_fused_io_ws, attn_ulysses_fused_trace,
-                       attn_ulysses_fused_ws,
+                       attn_ulysses_fused_noalloc, attn_ulysses_fused_ws,
                        dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
                        new_workspace, status_string, version, work_units, workspace_bytes,
                        workspace_count_bytes)

@@ -16,6 +16,8 @@ UA_ERR_ALIGN = -4
 UA_ERR_UNSUPPORTED = -5
 UA_ERR_HIP = -6
 UA_ERR_WORKSPACE = -7
+UA_ERR_SCRATCH = -8
+SCRATCH_BYTES = 128 << 20   # UA_SCRATCH_BYTES: fixed device scratch of attn_ulysses_fused_noalloc
 
 
 class UAError(RuntimeError):
@@ -55,6 +57,8 @@ def lib() -> ctypes.CDLL:
     sp = ctypes.POINTER(Shape)
     L.attn_ulysses_fused.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
     L.attn_ulysses_fused.restype = i
+    L.attn_ulysses_fused_noalloc.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
+    L.attn_ulysses_fused_noalloc.restype = i
     L.attn_serial.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
     L.attn_serial.restype = i
     L.a2a_permute.argtypes = [vp, i, i, vp, sp, vp]
@@ -334,3 +338,18 @@ def attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, out, workspace, scale=None, st
                                         _stream(stream, Xq, Xk, Xv, out, workspace))
     if st != UA_OK:
         raise UAError("attn_ulysses_fused_io_ws", st)
+
+
+def attn_ulysses_fused_noalloc(Q, K, V, rank, P, out, scale=None, stream=None):
+    """attn_ulysses_fused_ws with the workspace in the library's fixed device
+    scratch (SCRATCH_BYTES per GPU): allocates nothing.  Calls that overlap on
+    one GPU race on the scratch."""
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    st = lib().attn_ulysses_fused_noalloc(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
+                                          ctypes.byref(shp), scale, _stream(stream, Q, K, V, out))
+    if st != UA_OK:
+        raise UAError("attn_ulysses_fused_noalloc", st)

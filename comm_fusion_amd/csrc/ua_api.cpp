@@ -3,7 +3,8 @@
 // Host-side only: argument validation (no device access, so it runs on a
 // host without a GPU), placement set-up for the two epilogues, and launches.
 // The library allocates nothing and keeps no state between calls (the *_ws
-// calls use the workspace their caller passes in).
+// calls use the workspace their caller passes in; attn_ulysses_fused_noalloc
+// uses the library's fixed device scratch).
 
 #include "ulysses_attn.h"
 
@@ -157,6 +158,25 @@ int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
                           workspace, workspace_bytes);
 }
 
+int attn_ulysses_fused_noalloc(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                               const ua_shape *shp, float scale, hipStream_t stream)
+{
+    int64_t elems = 0;
+    int st = check_shape(shp, rank, P, &elems);
+    if (st != UA_OK) return st;
+    if (!isfinite(scale) || !(scale > 0.0f)) return UA_ERR_UNSUPPORTED;
+    if ((st = check_limits(shp, P)) != UA_OK) return st;
+    if (empty(shp)) return UA_OK;
+    if (!Q || !K || !V || !out) return UA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return UA_ERR_ALIGN;
+    const int64_t Hl = shp->H / P;
+    if (ua::workspace_bytes(shp->B, shp->S, Hl, (int)shp->d) > ua::kScratchBytes) return UA_ERR_SCRATCH;
+    const hipError_t e = ua::launch_attention_scratch((const uint16_t *)Q, (const uint16_t *)K,
+                                                      (const uint16_t *)V, shp->B, shp->S, Hl, (int)shp->d,
+                                                      scale, dest_placement(out, shp, rank, P), stream);
+    return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
 int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int rank, int P, void *out,
                              const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
                              hipStream_t stream)
@@ -265,6 +285,7 @@ const char *ua_status_string(int status)
     case UA_ERR_UNSUPPORTED: return "unsupported (d not 64/128, scale not finite and > 0, or shape beyond launch limits)";
     case UA_ERR_HIP: return "the HIP runtime reported an error";
     case UA_ERR_WORKSPACE: return "workspace smaller than ua_workspace_bytes";
+    case UA_ERR_SCRATCH: return "the shape's key split needs more than the library's fixed device scratch (UA_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }

@@ -49,6 +49,18 @@ hipError_t launch_permute(const uint16_t *o_local, int64_t B, int64_t S, int64_t
 hipError_t launch_gather(const Placement &in, int64_t B, int64_t S, int64_t Hl, int d,
                          uint16_t *x_local, hipStream_t stream);
 
+// Bytes of the fixed device scratch behind launch_attention_scratch.
+constexpr int64_t kScratchBytes = (int64_t)128 << 20;
+
+// launch_attention for the local-layout inputs with the key-split workspace
+// in the library's fixed device scratch of the current device (no
+// allocation; the caller checks workspace_bytes <= kScratchBytes).  Clears
+// the scratch's arrival counts with a kernel on `stream` first.  Calls that
+// overlap on one device race on the scratch.
+hipError_t launch_attention_scratch(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t B,
+                                    int64_t S, int64_t Hl, int d, float scale, const Placement &out,
+                                    hipStream_t stream);
+
 // Work units (one workgroup each) the attention launch uses for this shape
 // without a key split (query tiles).
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);

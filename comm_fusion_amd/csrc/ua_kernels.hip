@@ -59,6 +59,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1013,6 +1014,23 @@ __global__ __launch_bounds__(256) void gather_rows(Placement in, uint32_t n_chun
     *(u32x4 *)(dst + (int64_t)c * 8) = *(const u32x4 *)src;
 }
 
+// Zero n 16-byte chunks (the arrival counts of the fixed device scratch,
+// cleared before each call that uses it; a kernel rather than a memset, so
+// that the call can be captured into a HIP graph).
+__global__ __launch_bounds__(256) void zero_chunks(u32x4 *p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Fixed device scratch of the call that allocates nothing
+// (attn_ulysses_fused_noalloc): the key-split workspace (arrival counts, then
+// partial results) in a file-scope device array.  Every GPU the library runs
+// on holds one copy, at its own address, until the process ends.  Host code
+// must never pass this name to a kernel or a copy: it reaches the memory only
+// through the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 // Compute units and XCDs of the current device, queried once per device.
 // Without a device (the size queries run on hosts without a GPU) the full
 // MI355X is assumed: 256 CUs in 8 XCDs.  A failed query leaves no error
@@ -1045,6 +1063,29 @@ DeviceInfo device_info()
     g_dev_cus[dev].store(cus, std::memory_order_relaxed);
     g_dev_xcds[dev].store(xcds, std::memory_order_relaxed);
     return {cus, xcds};
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // Launch shape of the attention kernel for a problem: waves per workgroup,
@@ -1236,6 +1277,24 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     }
     void *args[] = {&a};
     return hipLaunchKernel(fn, dim3(a.n_units), dim3(64 * ls.nw), args, 0, stream);
+}
+
+hipError_t launch_attention_scratch(const uint16_t *q, const uint16_t *k, const uint16_t *v, int64_t B,
+                                    int64_t S, int64_t Hl, int d, float scale, const Placement &out,
+                                    hipStream_t stream)
+{
+    if (workspace_bytes(B, S, Hl, d) == 0)  // no split: the plain launch, no scratch
+        return launch_attention(q, k, v, Hl, 0, B, S, Hl, d, scale, out, stream);
+    void *ws = nullptr;
+    hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    // the counts must start at zero whatever an earlier call left behind
+    u32x4 *cnt = (u32x4 *)ws;
+    int n = (int)(kCountBytes / 16);
+    void *zargs[] = {(void *)&cnt, &n};
+    e = hipLaunchKernel((const void *)zero_chunks, dim3((n + 255) / 256), dim3(256), zargs, 0, stream);
+    if (e != hipSuccess) return e;
+    return launch_attention(q, k, v, Hl, 0, B, S, Hl, d, scale, out, stream, nullptr, ws);
 }
 
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,

@@ -86,8 +86,12 @@ enum {
     UA_ERR_ALIGN = -4,       /* a buffer pointer is not 16-byte aligned        */
     UA_ERR_UNSUPPORTED = -5, /* d not 64/128, scale not finite and > 0, too large */
     UA_ERR_HIP = -6,         /* the HIP runtime reported an error              */
-    UA_ERR_WORKSPACE = -7    /* workspace smaller than ua_workspace_bytes      */
+    UA_ERR_WORKSPACE = -7,   /* workspace smaller than ua_workspace_bytes      */
+    UA_ERR_SCRATCH = -8      /* split needs more than UA_SCRATCH_BYTES         */
 };
+
+/* Bytes of the fixed device scratch of attn_ulysses_fused_noalloc. */
+#define UA_SCRATCH_BYTES ((size_t)128 << 20)
 
 /*
  * Fused path (abstract; Fig. 5 steps d-e; Fig. 7 piggybacked pipeline):
@@ -155,6 +159,26 @@ int attn_serial_ws(const void *Q, const void *K, const void *V, int rank, int P,
 int attn_ulysses_fused_io_ws(const void *Xq, const void *Xk, const void *Xv, int rank, int P,
                              void *out, const ua_shape *shp, float scale, void *workspace,
                              size_t workspace_bytes, hipStream_t stream);
+/*
+ * attn_ulysses_fused_ws without a workspace argument and without allocating,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a fixed scratch array of UA_SCRATCH_BYTES (128 MiB) in device
+ * memory that the library holds on every GPU it runs on until the process
+ * ends; its address is looked up once per device, on the first call with
+ * that device current.  Each call first clears the scratch's arrival counts
+ * with a small kernel on `stream` (no memset), then runs exactly the launch
+ * of attn_ulysses_fused_ws: the output is bit-identical to that call's.
+ * Shapes that need no split run the plain launch and use no scratch.
+ * A shape whose ua_workspace_bytes exceeds UA_SCRATCH_BYTES gives
+ * UA_ERR_SCRATCH (checked after the other arguments, before any device
+ * access).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (different streams, or different host threads without
+ * ordering) race and may produce wrong output; stream-ordered calls are safe.
+ */
+int attn_ulysses_fused_noalloc(const void *Q, const void *K, const void *V, int rank, int P,
+                               void *out, const ua_shape *shp, float scale, hipStream_t stream);
+
 /* Workspace bytes the *_ws calls need for this shape (0: no split, or an
  * invalid or empty shape). */
 size_t ua_workspace_bytes(const ua_shape *shp, int P);

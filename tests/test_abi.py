@@ -38,7 +38,7 @@ def test_status_codes_match_header():
     text = open(HEADER).read()
     for name, val in [("UA_OK", 0), ("UA_ERR_NULL", -1), ("UA_ERR_SHAPE", -2), ("UA_ERR_RANK", -3),
                       ("UA_ERR_ALIGN", -4), ("UA_ERR_UNSUPPORTED", -5), ("UA_ERR_HIP", -6),
-                      ("UA_ERR_WORKSPACE", -7)]:
+                      ("UA_ERR_WORKSPACE", -7), ("UA_ERR_SCRATCH", -8)]:
         assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text)
         assert getattr(ua, name) == val
         assert ua.status_string(val) and ua.status_string(val) != "unknown status"
@@ -261,3 +261,24 @@ def test_workspace_validation():
         assert call(shape, P=8, out=O + 2, ws_bytes=0) == ua.UA_ERR_ALIGN
         # empty calls need nothing
         assert call((0, 16384, 24, 128), P=8, q=0, k=0, v=0, out=0, ws=0, ws_bytes=0) == ua.UA_OK
+
+
+def test_noalloc_validates_and_rejects_splits_beyond_its_scratch():
+    L = ua.lib()
+
+    def call(shape, rank=0, P=8, q=A, k=B_, v=C, out=O, scale=0.125):
+        return L.attn_ulysses_fused_noalloc(q, k, v, rank, P, out, ctypes.byref(Shape(*shape)), scale, None)
+
+    assert call((1, 4096, 24, 128), rank=8) == ua.UA_ERR_RANK
+    assert call((1, 4096, 24, 96)) == ua.UA_ERR_UNSUPPORTED
+    assert call((1, 4096, 24, 128), q=0) == ua.UA_ERR_NULL
+    assert call((1, 4096, 24, 128), out=O + 2) == ua.UA_ERR_ALIGN
+    assert call((0, 4096, 24, 128), q=0, k=0, v=0, out=0) == ua.UA_OK    # empty: nothing touched
+    # the heads of the video workload at 16384 keys split 4 ways over 320
+    # query tiles: ~165 MiB of partials, beyond the 128 MiB scratch
+    need = ua.workspace_bytes(1, 16384, 40, 128, 8)
+    assert need > ua.SCRATCH_BYTES == 128 << 20
+    assert call((1, 16384, 40, 128)) == ua.UA_ERR_SCRATCH
+    assert "scratch" in ua.status_string(ua.UA_ERR_SCRATCH)
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+UA_SCRATCH_BYTES\s+\(\(size_t\)128 << 20\)", text)
