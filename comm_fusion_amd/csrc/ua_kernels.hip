@@ -255,7 +255,11 @@ void attn_fwd(AttnArgs a)
     // in buffer j % 3).  Every LDS read in the main loop is an explicit
     // instruction (lds_b128, lds_tr16) with exact waits, so the compiler
     // needs no alias information about these buffers.
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[2 * KS * 3 * TILE];
+    // The same LDS later stages the normalised output rows of the NWG storing
+    // waves (RW rows of D bf16 each) for the row-coalesced epilogue stores.
+    constexpr int RING_BYTES = 2 * KS * 3 * TILE;
+    constexpr int STAGE_BYTES = NWG * RW * D * 2;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[RING_BYTES > STAGE_BYTES ? RING_BYTES : STAGE_BYTES];
     lds_u8 *const ks = (lds_u8 *)lds_all + grp * 3 * TILE;
     lds_u8 *const vs = (lds_u8 *)lds_all + (KS + grp) * 3 * TILE;
     using I0 = std::integral_constant<int, 0>;
@@ -372,12 +376,11 @@ void attn_fwd(AttnArgs a)
 
     // This lane's query row in each row block; rows past S (ragged last Q
     // tile) compute on row S-1 and are not stored.
-    int64_t s_q[RB];
     u32x4 qf[RB][KK];  // B operand of S^T = K Q^T: lane holds Q[s][16kk + 8g .. +7]
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        s_q[rb] = (int64_t)qt * BR + wq * RW + rb * 32 + il;
-        const int64_t s_ld = s_q[rb] < S ? s_q[rb] : S - 1;
+        const int64_t s_q = (int64_t)qt * BR + wq * RW + rb * 32 + il;
+        const int64_t s_ld = s_q < S ? s_q : S - 1;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
             qf[rb][kk] = *(const u32x4 *)(qh + s_ld * rs + 16 * kk + 8 * g);
@@ -889,24 +892,33 @@ void attn_fwd(AttnArgs a)
         }
     }
 
-    // ---- epilogue: normalise and store this lane's half of each of its
-    // rows straight into the destination slot (region p, row i, head g0 + h).
+    // ---- epilogue: normalise, round to bf16 and store every row straight
+    // into its destination slot (region p, row i, head g0 + h).  Each storing
+    // wave first stages its rows in the LDS (the K/V rings are free by now),
+    // then reads them back so that every store instruction writes whole
+    // rows: 16 lanes x 16 B per 256-byte row at d = 128 (4 rows per
+    // instruction), 8 lanes per 128-byte row at d = 64 (8 rows).  In the
+    // staging buffer the 16-byte chunk c of row r sits at position
+    // c ^ ((r / R256) % CPR), R256 rows per 256 bytes, so both the 8-byte
+    // writes (32 rows, one column chunk) and the row reads are spread over
+    // all LDS banks.
     float inv[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) inv[rb] = 1.0f / row_sum(l_run[rb]);
-    uint64_t tr_sb = 0;
-    if constexpr (TRACE) {
-        __syncthreads();
-        tr_sb = __builtin_amdgcn_s_memrealtime();
-    }
-    const Placement &o = a.out;
+    constexpr int ROWB = D * 2;      // bytes per output row
+    constexpr int CPR = ROWB / 16;   // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;    // rows per store instruction
+    constexpr int R256 = 256 / ROWB; // rows per 256 bytes of LDS
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+    lds_u8 *const stg = (lds_u8 *)lds_all + wq * RW * ROWB;
+    __syncthreads();  // every wave is done with the K/V rings and the key-group hand-off
+    if (grp == 0) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        if (s_q[rb] < S && grp == 0) {
-            const int64_t p = s_q[rb] / o.region_rows;
-            const int64_t i = s_q[rb] - p * o.region_rows;
-            uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + o.head0 + h) * D;
-            // O^T element r of block db is column db*32 + 8(r/4) + 4g + r%4.
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = rb * 32 + il;
+            const int sw = (row / R256) % CPR;
+            // O^T element r of block db is column db*32 + 8(r/4) + 4g + r%4:
+            // registers 4q4 .. 4q4+3 fill bytes 8g .. 8g+7 of chunk 4db + q4
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -914,8 +926,29 @@ void attn_fwd(AttnArgs a)
                     u32x2 w;
                     w[0] = pack_bf16(oacc[rb][db][4 * q4] * inv[rb], oacc[rb][db][4 * q4 + 1] * inv[rb]);
                     w[1] = pack_bf16(oacc[rb][db][4 * q4 + 2] * inv[rb], oacc[rb][db][4 * q4 + 3] * inv[rb]);
-                    *(u32x2 *)(dst + db * 32 + 8 * q4 + 4 * g) = w;
+                    *(lds_u32x2 *)(stg + row * ROWB + (((4 * db + q4) ^ sw) * 16) + 8 * g) = w;
                 }
+        }
+    }
+    __syncthreads();  // the staged rows are visible to every lane of their wave
+    uint64_t tr_sb = 0;
+    if constexpr (TRACE) tr_sb = __builtin_amdgcn_s_memrealtime();
+    const Placement &o = a.out;
+    if (grp == 0) {
+        const int chunk = lane % CPR;
+        const uint32_t rr = (uint32_t)o.region_rows;
+#pragma unroll
+        for (int j = 0; j < RW / RPI; ++j) {
+            const int row = j * RPI + lane / CPR;
+            const u32x4 val = *(const lds_u32x4 *)(stg + row * ROWB + ((chunk ^ ((row / R256) % CPR)) * 16));
+            const int64_t sq = (int64_t)qt * BR + wq * RW + row;
+            if (sq < S) {
+                // S < 2^31 rows: the region arithmetic fits 32 bits
+                const uint32_t p = (uint32_t)sq / rr;
+                const uint32_t i = (uint32_t)sq - p * rr;
+                uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + o.head0 + h) * D;
+                *(u32x4 *)(dst + chunk * 8) = val;
+            }
         }
     }
     if constexpr (TRACE) {
@@ -934,43 +967,42 @@ void attn_fwd(AttnArgs a)
 }
 
 // Epilogue stores alone: the attention kernel's grid, work-unit order and
-// per-lane store pattern (8-byte chunks of one row per lane, placed by the
-// same Placement arithmetic, RB row blocks per wave, only key group 0
-// storing), with a closed-form value instead of attention output: element
-// (s, head g, column c) gets bf16 bits (7s + 13g + 3c) & 0x3FFF (finite,
-// positive).  Measures what the destination layout sustains.
+// store pattern (whole rows, 16 bytes per lane, RPI rows per instruction,
+// each storing wave its RB*32 rows, only key group 0 storing), placed by the
+// same Placement arithmetic, with a closed-form value instead of attention
+// output: element (s, head g, column c) gets bf16 bits (7s + 13g + 3c) &
+// 0x3FFF (finite, positive).  Measures what the destination layout sustains.
 template <int D, int NW, int RB, int KS>
 __global__ __launch_bounds__(64 * NW) void epilogue_only(Placement o, int64_t S, int32_t Hl, int32_t n_qtiles,
                                                          int32_t n_units, int32_t n_xcd)
 {
+    constexpr int CPR = D * 2 / 16, RPI = 64 / CPR, RW = 32 * RB, BR = RW * NW / KS;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int il = lane & 31, g = lane >> 5;
     const int unit = xcd_unit(blockIdx.x, n_units, n_xcd);
     const int qt = unit % n_qtiles;
     const int bh = unit / n_qtiles;
     const int h = bh % Hl;
     const int64_t b = bh / Hl;
     if (wave >= NW / KS) return;
+    const int chunk = lane % CPR;
+    const uint32_t rr = (uint32_t)o.region_rows;
+    const int64_t gh = o.head0 + h;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int64_t s_q = (int64_t)qt * (32 * RB * NW / KS) + wave * (32 * RB) + rb * 32 + il;
+    for (int j = 0; j < RW / RPI; ++j) {
+        const int64_t s_q = (int64_t)qt * BR + wave * RW + j * RPI + lane / CPR;
         if (s_q >= S) continue;
-        const int64_t p = s_q / o.region_rows;
-        const int64_t i = s_q - p * o.region_rows;
-        const int64_t gh = o.head0 + h;
+        const uint32_t p = (uint32_t)s_q / rr;
+        const uint32_t i = (uint32_t)s_q - p * rr;
         uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + gh) * D;
         const unsigned base = (unsigned)(7 * s_q + 13 * gh);
+        u32x4 w;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const unsigned c = db * 32 + 8 * q4 + 4 * g;
-                u32x2 w;
-                w[0] = ((base + 3 * c) & 0x3FFFu) | (((base + 3 * (c + 1)) & 0x3FFFu) << 16);
-                w[1] = ((base + 3 * (c + 2)) & 0x3FFFu) | (((base + 3 * (c + 3)) & 0x3FFFu) << 16);
-                *(u32x2 *)(dst + c) = w;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const unsigned c = chunk * 8 + 2 * e;
+            w[e] = ((base + 3 * c) & 0x3FFFu) | (((base + 3 * (c + 1)) & 0x3FFFu) << 16);
+        }
+        *(u32x4 *)(dst + chunk * 8) = w;
     }
 }
 
