@@ -1,4 +1,6 @@
-"""fp64 CPU oracle for the fused Ulysses attention path (test infrastructure only).
+"""fp64 CPU oracles (test infrastructure only): the fused Ulysses attention
+path (``oracle.py`` over ``attn_oracle.c``) and the MoE expert path with its
+Combine exchange (``moe_oracle.py``, imported as ``oracle.moe_oracle``).
 
 Only ``tests/``, the smoke check and the benchmark's CPU-baseline leg import this
 package; the product library never does.
