@@ -1,7 +1,8 @@
 """Benchmark: fused Ulysses-shard attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--seq-len S]
-                    [--no-cpu] [--no-split] [--no-io] [--no-long] [--cpu-seconds T] [--rounds R]
+                    [--no-cpu] [--no-split] [--no-io] [--no-long] [--no-moe] [--cpu-seconds T]
+                    [--rounds R]
                     [--cpu-all] [--full-limit T] [--calibrate-copy MIB]
 
 One step = one attn_ulysses_fused call over the whole workload (attention over
@@ -31,6 +32,10 @@ Prints ONE JSON line:
   detail.long_configs  the same figures (timed region, medians, TFLOP/s and
             fraction of the bf16 peak, traced clock and DVFS flag) for each
             long-sequence workload: video_dit, dit_long and mixed;
+  detail.moe  the MoE expert path of one expert-parallel rank (DeepSeek-style
+            layer shape, balanced and skewed routing): the fused call under
+            the Expert-Wave and the interleaved schedule, the serial form
+            (experts, then a separate Combine scatter) and its halves;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -74,6 +79,8 @@ def parse():
                     help="skip the timings with the pre-attention exchange (detail.io)")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the other long-sequence workloads (detail.long_configs)")
+    ap.add_argument("--no-moe", action="store_true",
+                    help="skip the MoE expert path with the fused Combine (detail.moe)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--rounds", type=int, default=5,
@@ -449,6 +456,82 @@ class Case:
         return out
 
 
+MOE_CONFIGS = ("moe_ds", "moe_ds_skewed")
+MOE_WAVE = 4   # local experts per wave in the timed MoE calls
+
+
+class MoeCase:
+    """The MoE expert path of one rank at full size: tokens, routing and this
+    rank's expert weights resident in HBM, the Combine buffer, and the timed
+    callables (both schedules of the fused call, the serial form and its
+    halves)."""
+
+    def __init__(self, ua, torch, w, dev, weights=None):
+        from moe_inputs import moe_rank_weights, moe_tokens
+        self.w = w
+        x, idx, tw = moe_tokens(w)
+        self.weights = weights if weights is not None else moe_rank_weights(w, w.rank)
+        W1, W2 = self.weights
+        off, slots = ua.moe_recv_layout(idx, w.rank, w.P, w.hidden, w.inter, w.E)
+        self.N = int(off[-1])
+        self.rows_per_expert = np.diff(off)
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        dx, dW1, dW2 = up(x), up(W1), up(W2)
+        dtw = torch.from_numpy(tw).to(dev)
+        drs = torch.from_numpy(slots.astype(np.int32)).to(dev)
+        act = torch.empty(self.N * w.inter, dtype=torch.bfloat16, device=dev)
+        comb = torch.empty(w.P * w.T * w.k * w.hidden, dtype=torch.bfloat16, device=dev)
+        y = torch.empty(self.N * w.hidden, dtype=torch.bfloat16, device=dev)
+        G = MOE_WAVE
+
+        def fused(schedule):
+            return lambda: ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, comb, act,
+                                                  schedule=schedule, experts_per_wave=G)
+        alone = lambda: ua.moe_experts_local(dx, drs, dtw, off, dW1, dW2, w.P, w.E, y, act,  # noqa: E731
+                                             experts_per_wave=G)
+        scatter = lambda: ua.moe_combine_scatter(y, drs, self.N, w.P, w.T, w.hidden, w.inter, w.E, w.k,  # noqa: E731
+                                                 comb)
+
+        def serial():
+            alone()
+            scatter()
+
+        self.fns = {"interleaved": fused(ua.MOE_INTERLEAVED), "expert_wave": fused(ua.MOE_EXPERT_WAVE),
+                    "serial": serial, "experts_alone": alone, "scatter": scatter}
+        torch.cuda.synchronize()
+
+    def measure(self, warmup, rounds):
+        w = self.w
+        warm_up(self.fns["interleaved"], warmup, WARM_MS)
+        warm_up(self.fns["expert_wave"], 1, 50.0)
+        per = interleaved({"interleaved": self.fns["interleaved"]}, 1, 5)["interleaved"]
+        reps = max(2, min(500, int(100.0 / max(float(np.mean(per)), 1e-3)) + 1))
+        cmp = interleaved(self.fns, rounds, reps)
+        med = {k: float(np.median(v)) for k, v in cmp.items()}
+        flops = 6 * self.N * w.hidden * w.inter    # Linear-1 (2*inter outputs) + Linear-2, 2 flop per MAC
+        tf = lambda t: round(flops / (t * 1e-3) / 1e12, 2)  # noqa: E731
+        return {
+            "workload": w.name, "routing": w.routing, "P": w.P, "rank": w.rank, "T": w.T, "hidden": w.hidden,
+            "inter": w.inter, "E": w.E, "k": w.k, "rows_N": self.N,
+            "rows_per_expert_min_max": [int(self.rows_per_expert.min()), int(self.rows_per_expert.max())],
+            "experts_per_wave": MOE_WAVE, "flops": flops,
+            "interleaved_ms_median": round(med["interleaved"], 4),
+            "expert_wave_ms_median": round(med["expert_wave"], 4),
+            "speedup_interleaved_over_expert_wave": round(med["expert_wave"] / med["interleaved"], 4),
+            "serial_ms_median": round(med["serial"], 4),
+            "experts_alone_ms_median": round(med["experts_alone"], 4),
+            "scatter_ms_median": round(med["scatter"], 4),
+            "residual_interleaved_vs_alone": round((med["interleaved"] - med["experts_alone"]) / med["experts_alone"], 4),
+            "interleaved_TFLOPs": tf(med["interleaved"]),
+            "frac": round(flops / (med["interleaved"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "combine_bytes": self.N * w.hidden * 2,
+            "scatter_hbm_GBs": round(2 * self.N * w.hidden * 2 / (med["scatter"] * 1e-3) / 1e9, 1),
+        }
+
+
 def main():
     args = parse()
     if args.cpu_all:
@@ -471,6 +554,7 @@ def main():
         w = dataclasses.replace(w, name="%s_S%d" % (w.name, args.seq_len), S=args.seq_len, sampled=True)
         args.no_cpu = True
         args.no_long = True
+        args.no_moe = True
     dev = torch.device("cuda:0")
 
     if args.calibrate_copy:
@@ -577,6 +661,19 @@ def main():
             "kernel_code_sha256_16": source_digest(),
         },
     }
+    if not args.no_moe:
+        from moe_inputs import MOE_WORKLOADS
+        moe = {}
+        weights = None
+        for name in MOE_CONFIGS:
+            mw = MOE_WORKLOADS[name]
+            c = MoeCase(ua, torch, mw, dev, weights)
+            weights = c.weights if name == "moe_ds" else None   # moe_ds_skewed shares them
+            moe[name] = c.measure(args.warmup, args.rounds)
+            print(json.dumps({"moe": moe[name]}), file=sys.stderr, flush=True)
+            del c
+            torch.cuda.empty_cache()
+        out["detail"]["moe"] = moe
     if not args.no_cpu:
         Q, K, V = host
         out["cpu_baseline"] = cpu_baseline(w, Q, K, V, args.cpu_seconds)

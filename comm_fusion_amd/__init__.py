@@ -20,6 +20,11 @@ Names and arguments follow the C calls:
       (the _ws call with its workspace in the library's fixed device scratch)
   workspace_bytes(B, S, H, d, P), workspace_count_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
   new_workspace(B, S, H, d, P, device)  (a zeroed uint8 tensor, or None)
+the MoE expert path with the Combine fused into Linear-2 (include/moe_combine.h):
+  moe_recv_layout(topk_idx, rank, P, hidden, inter, E) -> (expert_offsets, row_slot)
+  moe_experts_combine(x, row_slot, topk_w, expert_offsets, W1, W2, P, E, combine, act,
+                      schedule=MOE_INTERLEAVED, experts_per_wave=4, stream=None)
+  moe_experts_local(...), moe_combine_scatter(...)   (the serial form)
 and, for measurement only,
   attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None)
   epilogue_store_only(B, S, H, d, rank, P, out, stream=None)
@@ -38,3 +43,5 @@ from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # no
                        dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
                        new_workspace, status_string, version, work_units, workspace_bytes,
                        workspace_count_bytes)
+from ._moe_binding import (MOE_EXPERT_WAVE, MOE_INTERLEAVED, MOE_MAX_WAVE, MoeShape,  # noqa: F401,E402
+                           moe_combine_scatter, moe_experts_combine, moe_experts_local, moe_recv_layout)

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libulysses_attn.so")
-SOURCES = ["ua_kernels.hip", "ua_api.cpp"]
+SOURCES = ["ua_kernels.hip", "ua_api.cpp", "moe_kernels.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -60,6 +60,13 @@ class MoeWorkload:
 def moe_tensors(w: MoeWorkload):
     """x [P][T][hidden] bf16 bits, topk_idx [P][T][k] int32, topk_w [P][T][k]
     float32, W1 [E_l][2*inter][hidden] and W2 [E_l][hidden][inter] bf16 bits."""
+    x, topk_idx, topk_w = moe_tokens(w)
+    W1, W2 = moe_rank_weights(w, w.rank)
+    return x, topk_idx, topk_w, W1, W2
+
+
+def moe_tokens(w: MoeWorkload):
+    """x [P][T][hidden] bf16 bits, topk_idx [P][T][k] int32, topk_w [P][T][k] float32."""
     rng = np.random.default_rng(w.seed)
     x = rng.standard_normal((w.P, w.T, w.hidden), dtype=np.float32)
     n_tok = w.P * w.T
@@ -77,8 +84,7 @@ def moe_tensors(w: MoeWorkload):
         raise ValueError(w.routing)
     topk_idx = idx.astype(np.int32).reshape(w.P, w.T, w.k)
     topk_w = rng.dirichlet(np.ones(w.k), size=n_tok).astype(np.float32).reshape(w.P, w.T, w.k)
-    W1, W2 = moe_rank_weights(w, w.rank)
-    return to_bf16_bits(x), topk_idx, topk_w, W1, W2
+    return to_bf16_bits(x), topk_idx, topk_w
 
 
 def moe_rank_weights(w: MoeWorkload, rank: int):
@@ -107,7 +113,8 @@ MOE_WORKLOADS = {
         MoeWorkload("moe_small_skewed", P=4, rank=0, T=512, hidden=1024, inter=512, E=32, k=4, seed=12,
                     routing="skewed"),
         MoeWorkload("moe_ds", P=8, rank=3, T=2048, hidden=7168, inter=2048, E=256, k=8, seed=13),
-        MoeWorkload("moe_ds_skewed", P=8, rank=3, T=2048, hidden=7168, inter=2048, E=256, k=8, seed=14,
+        # the same tokens and weights as moe_ds (same seed), skewed routing
+        MoeWorkload("moe_ds_skewed", P=8, rank=3, T=2048, hidden=7168, inter=2048, E=256, k=8, seed=13,
                     routing="skewed"),
     ]
 }

@@ -288,3 +288,15 @@ def test_store_checker_catches_a_barrier_before_the_wait():
     assert barriers_with_stores_in_flight(branch) == [(3, "s_barrier")]
     # plain (non-sc1) stores, such as the epilogue's, are not partials
     assert barriers_with_stores_in_flight(["global_store_dwordx2 v[0:1], v[2:3], off", "s_barrier"]) == []
+
+
+def test_moe_kernels_do_not_spill():
+    a = build.assembly("moe_kernels.hip")
+    names = re.findall(r"\.name:\s+(_Z\S*moe\S*)", a)
+    assert any("moe_tiles" in n for n in names), names
+    meta = re.findall(r"\.(vgpr_spill_count|sgpr_spill_count|private_segment_fixed_size):\s+(\d+)", a)
+    assert meta and all(int(v) == 0 for _, v in meta), meta
+    # two workgroups of 4 waves fit a CU: at most 256 VGPRs per wave, 64 KiB of LDS each
+    lds = [int(v) for v in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", a)]
+    vg = [int(v) for v in re.findall(r"\.vgpr_count:\s+(\d+)", a)]
+    assert max(lds) <= 65536 and max(vg) <= 256
