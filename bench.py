@@ -81,6 +81,8 @@ def parse():
                     help="skip the other long-sequence workloads (detail.long_configs)")
     ap.add_argument("--no-moe", action="store_true",
                     help="skip the MoE expert path with the fused Combine (detail.moe)")
+    ap.add_argument("--moe-wave", type=int, default=4, metavar="G",
+                    help="local experts per wave in the timed MoE calls")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--rounds", type=int, default=5,
@@ -457,7 +459,6 @@ class Case:
 
 
 MOE_CONFIGS = ("moe_ds", "moe_ds_skewed")
-MOE_WAVE = 4   # local experts per wave in the timed MoE calls
 
 
 class MoeCase:
@@ -466,9 +467,10 @@ class MoeCase:
     callables (both schedules of the fused call, the serial form and its
     halves)."""
 
-    def __init__(self, ua, torch, w, dev, weights=None):
+    def __init__(self, ua, torch, w, dev, G, weights=None):
         from moe_inputs import moe_rank_weights, moe_tokens
         self.w = w
+        self.G = G
         x, idx, tw = moe_tokens(w)
         self.weights = weights if weights is not None else moe_rank_weights(w, w.rank)
         W1, W2 = self.weights
@@ -485,7 +487,6 @@ class MoeCase:
         act = torch.empty(self.N * w.inter, dtype=torch.bfloat16, device=dev)
         comb = torch.empty(w.P * w.T * w.k * w.hidden, dtype=torch.bfloat16, device=dev)
         y = torch.empty(self.N * w.hidden, dtype=torch.bfloat16, device=dev)
-        G = MOE_WAVE
 
         def fused(schedule):
             return lambda: ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, comb, act,
@@ -517,7 +518,7 @@ class MoeCase:
             "workload": w.name, "routing": w.routing, "P": w.P, "rank": w.rank, "T": w.T, "hidden": w.hidden,
             "inter": w.inter, "E": w.E, "k": w.k, "rows_N": self.N,
             "rows_per_expert_min_max": [int(self.rows_per_expert.min()), int(self.rows_per_expert.max())],
-            "experts_per_wave": MOE_WAVE, "flops": flops,
+            "experts_per_wave": self.G, "flops": flops,
             "interleaved_ms_median": round(med["interleaved"], 4),
             "expert_wave_ms_median": round(med["expert_wave"], 4),
             "speedup_interleaved_over_expert_wave": round(med["expert_wave"] / med["interleaved"], 4),
@@ -667,7 +668,7 @@ def main():
         weights = None
         for name in MOE_CONFIGS:
             mw = MOE_WORKLOADS[name]
-            c = MoeCase(ua, torch, mw, dev, weights)
+            c = MoeCase(ua, torch, mw, dev, args.moe_wave, weights)
             weights = c.weights if name == "moe_ds" else None   # moe_ds_skewed shares them
             moe[name] = c.measure(args.warmup, args.rounds)
             print(json.dumps({"moe": moe[name]}), file=sys.stderr, flush=True)

@@ -32,6 +32,7 @@
 //    to bf16, stages the tile in the LDS and stores whole 256-byte row
 //    segments (16 bytes per lane) into each row's Combine slot.
 #include "moe_internal.h"
+#include "ua_internal.h"
 
 namespace moe {
 namespace {
@@ -71,6 +72,7 @@ struct MoeArgs {
     int32_t n_l1, n_l2;   // tiles of each kind in the launch
     int32_t k, hidden, inter;
     int32_t out_local;    // 1: Linear-2 writes receive row i (y_local); 0: its Combine slot
+    int32_t n_xcd;        // XCDs of the device
     const uint16_t *x;
     const int32_t *row_slot;
     const float *topk_w;
@@ -239,19 +241,30 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     }
 }
 
-// Block b of a launch with n_l2 Linear-2 and n_l1 Linear-1 tiles: the kinds
-// are dealt in proportion to their counts (block b is a Linear-2 tile when
-// floor((b+1) n_l2 / N) > floor(b n_l2 / N)), so in a mixed launch every
-// stretch of consecutive blocks holds both kinds; then the segment and its
-// (token tile, feature tile), feature tiles outermost so that neighbouring
-// blocks share the weight slice.
+// Workgroup i is dispatched to XCD i % nx; give each XCD a contiguous run
+// of the launch's tile sequence, so that the token tiles sharing a weight
+// slice (neighbours in the sequence) run on one XCD and share its L2.  A
+// bijection on [0, n).
+__device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t n, int64_t nx)
+{
+    const int64_t xcd = bid % nx, k = bid / nx;
+    const int64_t q = n / nx, r = n % nx;
+    return xcd < r ? xcd * (q + 1) + k : r * (q + 1) + (xcd - r) * q + k;
+}
+
+// Position b of the tile sequence of a launch with n_l2 Linear-2 and n_l1
+// Linear-1 tiles: the kinds are dealt in proportion to their counts
+// (position b is a Linear-2 tile when floor((b+1) n_l2 / N) > floor(b n_l2 /
+// N)), so in a mixed launch every stretch of the sequence holds both kinds;
+// then the segment and its (token tile, feature tile), feature tiles
+// outermost so that neighbours share the weight slice.
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void moe_tiles(MoeArgs a)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char lds_all[2 * STAGE];
     lds_u8 *const lds = (lds_u8 *)lds_all;
     const int64_t N = (int64_t)a.n_l1 + a.n_l2;
-    const int64_t b = blockIdx.x;
+    const int64_t b = xcd_block(blockIdx.x, N, a.n_xcd);
     const int64_t c2 = b * a.n_l2 / N, c2n = (b + 1) * a.n_l2 / N;
     const int kind = c2n > c2 ? 1 : 0;
     const int idx = kind ? (int)c2 : (int)(b - c2);
@@ -314,6 +327,7 @@ hipError_t launch_moe(const Problem &p, int schedule, int per_wave, bool local, 
     base.w2 = p.w2;
     base.act = p.act;
     base.out = p.out;
+    base.n_xcd = ua::device_xcd_count();
     const int n_waves = (int)((p.E_l + per_wave - 1) / per_wave);
     // kinds: bit 0 = Linear-1 of wave w1, bit 1 = Linear-2 of wave w2
     auto run = [&](int w1, int w2) -> hipError_t {

@@ -61,6 +61,10 @@ hipError_t launch_attention_scratch(const uint16_t *q, const uint16_t *k, const 
                                     int64_t S, int64_t Hl, int d, float scale, const Placement &out,
                                     hipStream_t stream);
 
+// XCDs of the current device (workgroups are dealt round robin over them);
+// 8, the full MI355X, on a host without a device.
+int device_xcd_count();
+
 // Work units (one workgroup each) the attention launch uses for this shape
 // without a key split (query tiles).
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);

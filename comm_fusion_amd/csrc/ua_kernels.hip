@@ -1249,6 +1249,8 @@ int64_t part_floats_per_split(const LaunchShape &ls, int d)
 
 }  // namespace
 
+int device_xcd_count() { return device_info().xcds; }
+
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 {
     const LaunchShape ls = launch_shape(B, S, Hl, d, device_info().cus);
