@@ -81,7 +81,7 @@ def parse():
                     help="skip the other long-sequence workloads (detail.long_configs)")
     ap.add_argument("--no-moe", action="store_true",
                     help="skip the MoE expert path with the fused Combine (detail.moe)")
-    ap.add_argument("--moe-wave", type=int, default=4, metavar="G",
+    ap.add_argument("--moe-wave", type=int, default=8, metavar="G",
                     help="local experts per wave in the timed MoE calls")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")

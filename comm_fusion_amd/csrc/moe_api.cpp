@@ -22,7 +22,7 @@ int check_moe_shape(const moe_shape *shp, int P)
 {
     if (!shp) return UA_ERR_NULL;
     const int64_t T = shp->T, hid = shp->hidden, inter = shp->inter, E = shp->E, k = shp->k;
-    if (P < 1 || T < 0 || hid < 128 || hid % 128 != 0 || inter < 64 || inter % 64 != 0 || E < 1 || E % P != 0 ||
+    if (P < 1 || T < 0 || hid < 256 || hid % 256 != 0 || inter < 128 || inter % 128 != 0 || E < 1 || E % P != 0 ||
         k < 1 || k > E)
         return UA_ERR_SHAPE;
     // 32-bit offsets inside the kernels: token rows of x, one expert's weights,

@@ -12,27 +12,30 @@
 // interleaved with wave w+1's Linear-1 tiles in one launch.
 //
 // Design for CDNA4:
-//  * one kernel for both layers: a workgroup of 4 wave64s computes a tile of
-//    128 output features x 128 token rows, each wave 64 x 64 as 2 x 2 blocks
-//    of v_mfma_f32_32x32x16_bf16, over k-steps of 64;
+//  * one kernel for both layers: a workgroup of 8 wave64s (two per SIMD)
+//    computes a tile of 256 output features x 256 token rows, each wave
+//    128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (six operand reads
+//    per eight MFMAs), over k-steps of 32;
 //  * outputs are computed transposed, C^T = W X^T: the weight rows are the A
 //    operand and the token rows the B operand, so every lane holds one token
 //    row and 16 of its features per block (runs of 4 consecutive features);
-//  * operand tiles go global -> VGPR -> LDS, double-buffered: the loads for
-//    step s+1 are in flight while step s computes; one barrier per step.  In
-//    the LDS a tile row (64 k values, 128 B) keeps its eight 16-byte chunks at
-//    positions chunk ^ ((row / 2) % 8), so both the row-wise stores and the
-//    fragment reads (32 rows, one chunk each) spread over all banks;
-//  * Linear-1 tiles take 64 gate rows and the 64 matching up rows of W1, so a
-//    wave's two feature blocks hold gate and up of the same intermediate
-//    columns and SiLU(gate) * up is formed in registers (bf16 out);
+//  * operand tiles go global -> LDS directly (no VGPR staging) through a
+//    ring of four stages, each copy issued three k-steps before its use; one
+//    barrier per step; the operand reads are explicit LDS instructions
+//    prefetched a k-substep ahead;
+//  * Linear-1 tiles take 128 gate rows and the 128 matching up rows of W1,
+//    arranged so that each wave's feature blocks hold gate and up of the
+//    same intermediate columns: SiLU(gate) * up is formed in registers;
 //  * token rows are gathered through row_slot (slot / k is the token), so the
 //    dispatch exchange's receive side is read in place;
 //  * the Linear-2 epilogue multiplies each row by its routing weight, rounds
-//    to bf16, stages the tile in the LDS and stores whole 256-byte row
+//    to bf16, stages the tile in the LDS and stores whole 512-byte row
 //    segments (16 bytes per lane) into each row's Combine slot.
 #include "moe_internal.h"
 #include "ua_internal.h"
+
+#include <type_traits>
+#include <utility>
 
 namespace moe {
 namespace {
@@ -47,13 +50,20 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
-constexpr int BM = 128;                 // token rows per tile
-constexpr int BK = 64;                  // k per step
-constexpr int NT = 256;                 // threads per workgroup (4 waves)
-constexpr int TILE = 128 * BK * 2;      // bytes of one operand tile (16 KiB)
-constexpr int STAGE = 2 * TILE;         // W tile + token tile
-constexpr int L1_COLS = 64;             // intermediate columns per Linear-1 tile
-constexpr int L2_COLS = 128;            // hidden columns per Linear-2 tile
+constexpr int BM = 256;                 // token rows per tile
+constexpr int BF = 256;                 // feature rows per tile (Linear-1: 128 gate + 128 up)
+constexpr int BK = 32;                  // k per step
+constexpr int NSTAGE = 4;               // LDS ring: copies run three steps ahead
+constexpr int NW = 8;                   // waves per workgroup (two per SIMD)
+constexpr int NT = 64 * NW;
+constexpr int TILE = 256 * BK * 2;      // bytes of one operand tile (16 KiB)
+constexpr int STAGE = 2 * TILE;         // W tile + token tile (32 KiB)
+constexpr int NCPW = TILE / 1024 / NW;  // 1 KiB copies per wave per operand tile
+constexpr int L1_COLS = 128;            // intermediate columns per Linear-1 tile
+constexpr int L2_COLS = 256;            // hidden columns per Linear-2 tile
+
+typedef const __attribute__((address_space(1))) void gbl_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // One expert's tiles of one kind in a launch.
 struct Seg {
@@ -91,15 +101,43 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// Position of 16-byte chunk c of tile row r in the LDS (see the file comment).
-__device__ __forceinline__ int lds_pos(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// MFMA operand reads from the LDS as explicit instructions with
+// compile-time offsets, each waited for exactly (lgkm_wait) before the MFMAs
+// that consume it: the compiler does not see them, so it inserts no waits of
+// its own -- none on the global->LDS copies into the other stage, which it
+// could not tell apart from these reads.  The wait is tied to the fragment
+// registers, so nothing may copy or reuse them before it.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read(unsigned addr)
+{
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+    return r;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4 (&fa)[4], u32x4 (&fb)[2])
+{
+    asm volatile("s_waitcnt lgkmcnt(%6)"
+                 : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1])
+                 : "i"(N));
+}
 
+// One output tile: 256 features x 256 token rows, K in steps of 32.
+// Operand tiles in the LDS: [row][64 B] (the step's 32 k values), the four
+// 16-byte chunks of a row at positions chunk ^ ((row / 4) % 4), so a
+// fragment read (32 rows, one chunk each per half-wave) spreads over all
+// banks.  They are filled by 1 KiB global->LDS copies (lane L of copy c
+// lands at byte 1024 c + 16 L: row 16 c + L / 4, fetching chunk
+// (L % 4) ^ ((L / 16) % 4)) into a ring of four stages: the copies of step
+// s+3 are issued as step s starts, so each has three steps to land.  Wave
+// (wf, wt) computes features 128 wf .. +127 (four 32-row blocks) of token
+// rows 64 wt .. +63 (two).
 template <int KIND>
 __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int n, lds_u8 *lds)
 {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wf = wave & 1, wt = wave >> 1;  // feature half, token half of the tile
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wf = wave & 1, wt = wave >> 1;
     const int l32 = lane & 31, g = lane >> 5;
     const int K = KIND == 0 ? a.hidden : a.inter;
     const int nk = K / BK;
@@ -107,130 +145,178 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
                                                  : a.w2 + (int64_t)sg.expert * a.hidden * a.inter);
     const char *bbase = (const char *)(KIND == 0 ? a.x : a.act);
 
-    // This thread's share of each operand tile: rows rr + 32 i (i < 4),
-    // 16-byte chunk kc of the step's 64 k values.
-    const int rr = tid >> 3, kc = tid & 7;
-    unsigned aoff[4], boff[4];
+    // This wave's copies: numbers NCPW wave .. of each operand tile.
+    const unsigned chunk16 = (unsigned)((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+    unsigned aoff[NCPW], boff[NCPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = rr + 32 * i;
-        // weight row of tile row r: Linear-1 takes gate rows 64n .. 64n+63 and
-        // up rows inter + 64n .. ; Linear-2 takes hidden rows 128n .. 128n+127
-        const int wrow = KIND == 0 ? (r < 64 ? L1_COLS * n + r : a.inter + L1_COLS * n + r - 64) : L2_COLS * n + r;
-        aoff[i] = ((unsigned)wrow * (unsigned)K + kc * 8) * 2;
+    for (int i = 0; i < NCPW; ++i) {
+        const int c = NCPW * wave + i;
+        const int r = 16 * c + (lane >> 2);
+        // weight row of tile row r: Linear-1 rows 128 h .. 128 h + 63 are gate
+        // rows 128 n + 64 h .., rows 128 h + 64 .. the matching up rows, so a
+        // wave's feature blocks 0, 1 (gate) and 2, 3 (up) hold the same
+        // intermediate columns; Linear-2 takes hidden rows 256 n + r
+        const int h = r >> 7, q = r & 127;
+        const int wrow = KIND == 0 ? (q < 64 ? L1_COLS * n + 64 * h + q : a.inter + L1_COLS * n + 64 * h + q - 64)
+                                   : L2_COLS * n + r;
+        aoff[i] = (unsigned)wrow * (unsigned)K * 2 + chunk16;
         // token row: rows past the expert's end repeat its last row (not stored)
         const int rl = m * BM + r < sg.rows ? m * BM + r : sg.rows - 1;
         const int ri = sg.row0 + rl;
         const unsigned brow = KIND == 0 ? (unsigned)(a.row_slot[ri] / a.k) : (unsigned)ri;
-        boff[i] = (brow * (unsigned)K + kc * 8) * 2;
+        boff[i] = brow * (unsigned)K * 2 + chunk16;
     }
-    const int spos = lds_pos(rr, kc);  // the same for rr + 32 i (the swizzle has period 16)
-
-    u32x4 ra[4], rb[4];
-    auto load = [&](int s) {
+    auto copy = [&](int s, int st) {
         const unsigned ko = (unsigned)s * BK * 2;
+        lds_u8 *dst = lds + st * STAGE + NCPW * wave * 1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = *(const u32x4 *)(wbase + aoff[i] + ko);
-            rb[i] = *(const u32x4 *)(bbase + boff[i] + ko);
-        }
-    };
-    auto store = [&](int st) {
-        lds_u8 *s = lds + st * STAGE;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *(lds_u32x4 *)(s + spos + i * 32 * 128) = ra[i];
-            *(lds_u32x4 *)(s + TILE + spos + i * 32 * 128) = rb[i];
+        for (int i = 0; i < NCPW; ++i) {
+            __builtin_amdgcn_global_load_lds((gbl_void *)(wbase + aoff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko), (lds_void *)(dst + TILE + i * 1024),
+                                             16, 0, 0);
         }
     };
 
-    f32x16 acc[2][2];
+    // Per-lane LDS addresses of the fragment reads; stage and block are
+    // instruction offsets (stages 2 and 3 through their own base registers:
+    // the offset field holds 16 bits).  Fragment element layout: lane l gives
+    // row (block + l % 32), k values 8 (l / 32) .. +7 of the 16-wide
+    // k-substep (substep 0: chunks 0, 1; substep 1: chunks 2, 3).
+    const unsigned lbase = (unsigned)(uintptr_t)lds;
+    const unsigned sw0 = (unsigned)(((0 + g) ^ ((l32 >> 2) & 3)) * 16);
+    const unsigned sw1 = (unsigned)(((2 + g) ^ ((l32 >> 2) & 3)) * 16);
+    const unsigned ra = lbase + (unsigned)(128 * wf + l32) * 64;
+    const unsigned rb = lbase + TILE + (unsigned)(64 * wt + l32) * 64;
+    // [stage / 2][substep]
+    const unsigned abase[2][2] = {{ra + sw0, ra + sw1}, {ra + 2 * STAGE + sw0, ra + 2 * STAGE + sw1}};
+    const unsigned bbase2[2][2] = {{rb + sw0, rb + sw1}, {rb + 2 * STAGE + sw0, rb + 2 * STAGE + sw1}};
+
+    f32x16 acc[4][2];
 #pragma unroll
-    for (int fb = 0; fb < 2; ++fb)
+    for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
-    // tile rows of the wave's feature blocks: Linear-1 pairs the gate block
-    // (rows 32 wf ..) with the up block of the same columns (rows 64 + 32 wf ..)
-    const int frow0 = KIND == 0 ? 32 * wf : 64 * wf;
-    const int fstep = KIND == 0 ? 64 : 32;
-    const int trow0 = 64 * wt;
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk) load(s + 1);
-        const lds_u8 *st = lds + (s & 1) * STAGE;
+    u32x4 fa[2][4], fbr[2][2];
+    // the six fragment reads of k-substep KK (0, 1) of the stage ST
+    auto reads = [&](auto stc, auto kkc, u32x4 (&da)[4], u32x4 (&db)[2]) {
+        constexpr int ST = decltype(stc)::value, KK = decltype(kkc)::value;
+        constexpr int OFF = (ST & 1) * STAGE;
+        const unsigned pa = abase[ST >> 1][KK], pb = bbase2[ST >> 1][KK];
+        da[0] = lds_read<OFF + 0 * 2048>(pa);
+        da[1] = lds_read<OFF + 1 * 2048>(pa);
+        da[2] = lds_read<OFF + 2 * 2048>(pa);
+        da[3] = lds_read<OFF + 3 * 2048>(pa);
+        db[0] = lds_read<OFF + 0 * 2048>(pb);
+        db[1] = lds_read<OFF + 1 * 2048>(pb);
+    };
+    auto mfmas = [&](u32x4 (&da)[4], u32x4 (&db)[2]) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + g;
-            u32x4 af[2], bf[2];
+        for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-            for (int fb = 0; fb < 2; ++fb) af[fb] = *(const lds_u32x4 *)(st + lds_pos(frow0 + fstep * fb + l32, c));
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) bf[tb] = *(const lds_u32x4 *)(st + TILE + lds_pos(trow0 + 32 * tb + l32, c));
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, af[fb]), __builtin_bit_cast(bf16x8, bf[tb]), acc[fb][tb], 0, 0, 0);
-        }
-        if (s + 1 < nk) store((s + 1) & 1);
-        __syncthreads();
+            for (int tb = 0; tb < 2; ++tb)
+                acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, da[fb]), __builtin_bit_cast(bf16x8, db[tb]), acc[fb][tb], 0, 0, 0);
+    };
+    // One k-step on stage ST = s % 4.  Its copies have landed once at most
+    // the later steps' copies already issued (those of s+1 and s+2, 2 NCPW
+    // each) remain in flight; after the barrier every wave is done with step
+    // s-1, whose stage takes the copies of step s+3.
+    auto step = [&](int s, auto stc) {
+        constexpr int ST = decltype(stc)::value;
+        const int later = nk - 1 - s;   // steps after s
+        if (later >= 2)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(4 * NCPW) : "memory");
+        else if (later == 1)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(2 * NCPW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + 3 < nk) copy(s + 3, (ST + 3) & 3);
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        reads(stc, I0(), fa[0], fbr[0]);
+        reads(stc, I1(), fa[1], fbr[1]);
+        lgkm_wait<6>(fa[0], fbr[0]);
+        mfmas(fa[0], fbr[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait<0>(fa[1], fbr[1]);
+        mfmas(fa[1], fbr[1]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: the copies of steps 0, 1, 2
+    for (int p = 0; p < 3 && p < nk; ++p) copy(p, p);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    int s = 0;
+    for (; s + 3 < nk; s += 4) {
+        step(s, S0());
+        step(s + 1, S1());
+        step(s + 2, S2());
+        step(s + 3, S3());
     }
+    if (s < nk) step(s++, S0());
+    if (s < nk) step(s++, S1());
+    if (s < nk) step(s++, S2());
+    // every wave is done with the operand tiles (the Linear-2 epilogue reuses the LDS)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // Accumulator register r of block (fb, tb) is feature 8(r/4) + 4g + r%4 of
     // the block, token row l32 of the block.
     if constexpr (KIND == 0) {
-        // SiLU(gate) * up -> act[row][64n + 32 wf + ...], bf16
+        // SiLU(gate) * up -> act[row][128 n + 64 wf + ...], bf16
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const int rl = m * BM + trow0 + 32 * tb + l32;
+            const int rl = m * BM + 64 * wt + 32 * tb + l32;
             if (rl >= sg.rows) continue;
-            uint16_t *dst = a.act + (int64_t)(sg.row0 + rl) * a.inter + L1_COLS * n + 32 * wf + 4 * g;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                float v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = silu(acc[0][tb][4 * q4 + e]) * acc[1][tb][4 * q4 + e];
-                u32x2 w;
-                w[0] = pack_bf16(v[0], v[1]);
-                w[1] = pack_bf16(v[2], v[3]);
-                *(u32x2 *)(dst + 8 * q4) = w;
-            }
-        }
-    } else {
-        // weighted rows, staged as [token row][128 features] (chunk c of row
-        // r at position c ^ (r % 16)), then stored as whole 256-byte segments
-        float wrow[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int rl = m * BM + trow0 + 32 * tb + l32;
-            wrow[tb] = rl < sg.rows ? a.topk_w[a.row_slot[sg.row0 + rl]] : 0.f;
-        }
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int tr = trow0 + 32 * tb + l32;
+            uint16_t *dst = a.act + (int64_t)(sg.row0 + rl) * a.inter + L1_COLS * n + 64 * wf + 4 * g;
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int c = 8 * wf + 4 * fb + q4;
+                    float v[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = silu(acc[fb][tb][4 * q4 + e]) * acc[fb + 2][tb][4 * q4 + e];
+                    u32x2 w;
+                    w[0] = pack_bf16(v[0], v[1]);
+                    w[1] = pack_bf16(v[2], v[3]);
+                    *(u32x2 *)(dst + 32 * fb + 8 * q4) = w;
+                }
+        }
+    } else {
+        // weighted rows, staged as [token row][256 features] (chunk c of row
+        // r at position c ^ (r % 32)), then stored as whole 512-byte rows
+        float wrow[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int rl = m * BM + 64 * wt + 32 * tb + l32;
+            wrow[tb] = rl < sg.rows ? a.topk_w[a.row_slot[sg.row0 + rl]] : 0.f;
+        }
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int tr = 64 * wt + 32 * tb + l32;
+#pragma unroll
+            for (int fb = 0; fb < 4; ++fb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int c = 16 * wf + 4 * fb + q4;
                     u32x2 w;
                     w[0] = pack_bf16(acc[fb][tb][4 * q4] * wrow[tb], acc[fb][tb][4 * q4 + 1] * wrow[tb]);
                     w[1] = pack_bf16(acc[fb][tb][4 * q4 + 2] * wrow[tb], acc[fb][tb][4 * q4 + 3] * wrow[tb]);
-                    *(lds_u32x2 *)(lds + tr * 256 + ((c ^ (tr & 15)) << 4) + 8 * g) = w;
+                    *(lds_u32x2 *)(lds + tr * 512 + ((c ^ (tr & 31)) << 4) + 8 * g) = w;
                 }
         }
         __syncthreads();
-        const int chunk = lane & 15;
+        const int chunk = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int tr = 32 * wave + 4 * j + (lane >> 4);
-            const u32x4 v = *(const lds_u32x4 *)(lds + tr * 256 + ((chunk ^ (tr & 15)) << 4));
+        for (int j = 0; j < 16; ++j) {
+            const int tr = 32 * wave + 2 * j + (lane >> 5);
+            const u32x4 v = *(const lds_u32x4 *)(lds + tr * 512 + ((chunk ^ (tr & 31)) << 4));
             const int rl = m * BM + tr;
             if (rl < sg.rows) {
                 const int ri = sg.row0 + rl;
@@ -261,7 +347,7 @@ __device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t n, int64_t nx)
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void moe_tiles(MoeArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[NSTAGE * STAGE];  // 128 KiB: one workgroup per CU
     lds_u8 *const lds = (lds_u8 *)lds_all;
     const int64_t N = (int64_t)a.n_l1 + a.n_l2;
     const int64_t b = xcd_block(blockIdx.x, N, a.n_xcd);

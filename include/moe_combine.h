@@ -34,7 +34,7 @@
  *            to local expert e, and row i serves slot row_slot[i] =
  *            (p*T + t)*k + j (token p*T + t, choice j);
  *   act      [N][inter] bf16 workspace (Linear-1 output, caller-owned).
- * Sizes: hidden % 128 == 0, inter % 64 == 0, P*T*hidden*2 < 2^32 bytes,
+ * Sizes: hidden % 256 == 0, inter % 128 == 0, P*T*hidden*2 < 2^32 bytes,
  * 2*inter*hidden*2 < 2^32 bytes (one expert's W1).
  *
  * Ownership: the caller allocates and frees every buffer; the library
@@ -60,8 +60,8 @@ extern "C" {
 
 typedef struct {
     int64_t T;      /* tokens per rank                  (>= 0)              */
-    int64_t hidden; /* model width                      (>= 128, % 128 == 0) */
-    int64_t inter;  /* expert intermediate size         (>= 64, % 64 == 0)   */
+    int64_t hidden; /* model width                      (>= 256, % 256 == 0) */
+    int64_t inter;  /* expert intermediate size         (>= 128, % 128 == 0) */
     int64_t E;      /* experts over all ranks           (>= 1, E % P == 0)   */
     int64_t k;      /* experts per token                (1 .. E)            */
 } moe_shape;

@@ -155,7 +155,7 @@ def test_ragged_and_empty_experts():
 
 
 def test_no_rows_routed_here_writes_nothing():
-    w = MoeWorkload("moe_none", P=2, rank=1, T=16, hidden=128, inter=64, E=4, k=1, seed=32)
+    w = MoeWorkload("moe_none", P=2, rank=1, T=16, hidden=256, inter=128, E=4, k=1, seed=32)
     x, idx, tw, W1, W2 = moe_tensors(w)
     idx[:] = 0                                    # every token chose an expert of rank 0
     c = Case(w, (x, idx, tw, W1, W2))

@@ -34,13 +34,14 @@ def _operands(line: str):
     return parts[0], [o.strip().split()[0] for o in parts[1].split(",") if o.strip()]
 
 
-def _kernel_bodies(asm: str):
-    """{kernel symbol: [instruction and label lines]} for the attention kernels."""
+def _kernel_bodies(asm: str, kernel: str = "attn_fwd"):
+    """{kernel symbol: [instruction and label lines]} for the kernels whose
+    symbol contains `kernel` (default: the attention kernels)."""
     out = {}
     name = None
     for raw in asm.splitlines():
         line = raw.split(";")[0].strip()
-        m = re.match(r"^(_Z\S*attn_fwd\S*):$", line)
+        m = re.match(r"^(_Z\S*%s\S*):$" % kernel, line)
         if m:
             name = m.group(1)
             out[name] = []
@@ -296,7 +297,18 @@ def test_moe_kernels_do_not_spill():
     assert any("moe_tiles" in n for n in names), names
     meta = re.findall(r"\.(vgpr_spill_count|sgpr_spill_count|private_segment_fixed_size):\s+(\d+)", a)
     assert meta and all(int(v) == 0 for _, v in meta), meta
-    # two workgroups of 4 waves fit a CU: at most 256 VGPRs per wave, 64 KiB of LDS each
+    # one workgroup of 8 waves per CU, two waves per SIMD: at most 256 VGPRs
+    # per wave and the CU's 160 KiB of LDS
     lds = [int(v) for v in re.findall(r"\.group_segment_fixed_size:\s+(\d+)", a)]
     vg = [int(v) for v in re.findall(r"\.vgpr_count:\s+(\d+)", a)]
-    assert max(lds) <= 65536 and max(vg) <= 256
+    assert max(lds) <= 160 * 1024 and max(vg) <= 256
+
+
+def test_moe_lds_results_not_used_before_their_wait():
+    # the MoE kernel reads its MFMA operands with the same explicit LDS reads
+    bodies = _kernel_bodies(build.assembly("moe_kernels.hip"), "moe_tiles")
+    assert len(bodies) == 1, sorted(bodies)
+    for name, lines in bodies.items():
+        assert sum(l.startswith("ds_read_b128") for l in lines) >= 48, name
+        bad = early_uses(lines)
+        assert not bad, "%s: %s" % (name, bad[:5])

@@ -41,8 +41,8 @@ def test_experts_call_validation():
     ok = MoeShape(64, 256, 128, 8, 2)      # T, hidden, inter, E, k
     off = [0, 3, 3, 10, 12]                # E/P = 4 local experts (P = 2)
     assert _combine(None, off) == ua.UA_ERR_NULL
-    assert _combine(MoeShape(64, 200, 128, 8, 2), off) == ua.UA_ERR_SHAPE      # hidden % 128
-    assert _combine(MoeShape(64, 256, 96, 8, 2), off) == ua.UA_ERR_SHAPE       # inter % 64
+    assert _combine(MoeShape(64, 384, 128, 8, 2), off) == ua.UA_ERR_SHAPE      # hidden % 256
+    assert _combine(MoeShape(64, 256, 192, 8, 2), off) == ua.UA_ERR_SHAPE      # inter % 128
     assert _combine(MoeShape(64, 256, 128, 7, 2), off) == ua.UA_ERR_SHAPE      # E % P
     assert _combine(MoeShape(64, 256, 128, 8, 9), off) == ua.UA_ERR_SHAPE      # k > E
     assert _combine(ok, off, schedule=2) == ua.UA_ERR_UNSUPPORTED
@@ -77,13 +77,13 @@ def test_recv_layout_matches_the_oracle_slots(name):
 
 
 def test_recv_layout_rejects_bad_expert_ids_and_small_capacity():
-    w = MoeWorkload("t", P=2, rank=0, T=4, hidden=128, inter=64, E=4, k=2, seed=1)
+    w = MoeWorkload("t", P=2, rank=0, T=4, hidden=256, inter=128, E=4, k=2, seed=1)
     _, idx, _, _, _ = moe_tensors(w)
     bad = idx.copy()
     bad[1, 2, 1] = 4
     with pytest.raises(ua.UAError):
-        ua.moe_recv_layout(bad, 0, 2, 128, 64, 4)
-    shp = MoeShape(4, 128, 64, 4, 2)
+        ua.moe_recv_layout(bad, 0, 2, 256, 128, 4)
+    shp = MoeShape(4, 256, 128, 4, 2)
     off = np.zeros(3, np.int64)
     slots = np.zeros(1, np.int32)
     st = _lib().moe_recv_layout(idx.ctypes.data, 0, 2, ctypes.byref(shp), off.ctypes.data, slots.ctypes.data, 1)
