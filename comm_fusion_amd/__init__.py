@@ -18,7 +18,8 @@ Names and arguments follow the C calls:
   attn_ulysses_fused_io_ws(Xq, Xk, Xv, rank, P, out, workspace, scale=None, stream=None)
   attn_ulysses_fused_noalloc(Q, K, V, rank, P, out, scale=None, stream=None)
       (the _ws call with its workspace in the library's fixed device scratch)
-  workspace_bytes(B, S, H, d, P), workspace_count_bytes(B, S, H, d, P), key_split(B, S, H, d, P)
+  workspace_bytes(B, S, H, d, P), workspace_count_bytes(B, S, H, d, P), key_split(B, S, H, d, P),
+  stream_k_iters(B, S, H, d, P)
   new_workspace(B, S, H, d, P, device)  (a zeroed uint8 tensor, or None)
 the MoE expert path with the Combine fused into Linear-2 (include/moe_combine.h):
   moe_recv_layout(topk_idx, rank, P, hidden, inter, E) -> (expert_offsets, row_slot)
@@ -41,7 +42,7 @@ from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # no
                        attn_ulysses_fused_io, attn_ulysses_fused_io_ws, attn_ulysses_fused_trace,
                        attn_ulysses_fused_noalloc, attn_ulysses_fused_ws,
                        dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
-                       new_workspace, status_string, version, work_units, workspace_bytes,
+                       new_workspace, status_string, stream_k_iters, version, work_units, workspace_bytes,
                        workspace_count_bytes)
 from ._moe_binding import (MOE_EXPERT_WAVE, MOE_INTERLEAVED, MOE_MAX_WAVE, MoeShape,  # noqa: F401,E402
                            moe_combine_scatter, moe_experts_combine, moe_experts_local, moe_recv_layout)

@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.ua_workspace_count_bytes.restype = sz
     L.ua_key_split.argtypes = [sp, i]
     L.ua_key_split.restype = i
+    L.ua_stream_k_iters.argtypes = [sp, i]
+    L.ua_stream_k_iters.restype = ctypes.c_int64
     _lib = L
     return L
 
@@ -271,6 +273,12 @@ def workspace_bytes(B, S, H, d, P) -> int:
 def workspace_count_bytes(B, S, H, d, P) -> int:
     """Leading workspace bytes that hold the arrival counts (zero between calls)."""
     return int(lib().ua_workspace_count_bytes(ctypes.byref(Shape(B, S, H, d)), int(P)))
+
+
+def stream_k_iters(B, S, H, d, P) -> int:
+    """(query tile, key tile) iterations per workgroup of a stream-K split in
+    the *_ws calls (0: the plain key split, or none)."""
+    return int(lib().ua_stream_k_iters(ctypes.byref(Shape(B, S, H, d)), int(P)))
 
 
 def key_split(B, S, H, d, P) -> int:

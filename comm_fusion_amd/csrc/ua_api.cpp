@@ -201,6 +201,14 @@ size_t ua_workspace_count_bytes(const ua_shape *shp, int P)
     return (size_t)ua::workspace_count_bytes(shp->B, shp->S, shp->H / P, (int)shp->d);
 }
 
+int64_t ua_stream_k_iters(const ua_shape *shp, int P)
+{
+    int64_t elems = 0;
+    if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
+    if (empty(shp)) return 0;
+    return ua::stream_k_iters(shp->B, shp->S, shp->H / P, (int)shp->d);
+}
+
 int ua_key_split(const ua_shape *shp, int P)
 {
     int64_t elems = 0;

@@ -72,6 +72,9 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);
 // Workgroups per query tile of a launch given a workspace (1: no split), and
 // the workspace bytes that launch needs (0 when it does not split).
 int key_split(int64_t B, int64_t S, int64_t Hl, int d);
+// Iterations (query tile, key tile) per workgroup when that split is
+// stream-K (one workgroup per CU); 0 otherwise.
+int64_t stream_k_iters(int64_t B, int64_t S, int64_t Hl, int d);
 int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d);
 // Leading bytes of that workspace that hold the arrival counts.
 int64_t workspace_count_bytes(int64_t B, int64_t S, int64_t Hl, int d);

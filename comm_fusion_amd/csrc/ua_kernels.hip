@@ -99,9 +99,13 @@ struct AttnArgs {
     // key split across workgroups (XS builds only): n_split workgroups per
     // query tile, each on a run of about 1/n_split of the keys; their partial
     // results meet in ws_part, and ws_cnt counts arrivals per query tile
-    int32_t n_split;
+    int32_t n_split;   // parts per query tile (stream-K: the most any query tile has)
     float *ws_part;
     unsigned *ws_cnt;
+    // stream-K (XS builds): iterations per workgroup (0: split as above) and
+    // the query tiles of the launch, B*Hl*n_qtiles
+    int32_t sk_iters;
+    int32_t n_units_q;
 };
 
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
@@ -264,17 +268,25 @@ void attn_fwd(AttnArgs a)
     lds_u8 *const vs = (lds_u8 *)lds_all + (KS + grp) * 3 * TILE;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+
+    // One work item: query tile qt of (batch, local head) bh over ntl key
+    // tiles per key group, key group g starting at key tile kt0 + g*ntl; in
+    // XS builds it is part `part` of the `nparts` parts of the query tile's
+    // keys (parts in key order), whose partial results meet in the
+    // workspace.  `unit` names the item in the measurement build's trace.
+    auto run = [&](const int unit, const int qt, const int bh, const int kt0, const int ntl, const int part,
+                   const int nparts) {
+    // The per-lane indices (and every address derived from them) are formed
+    // anew for each work item from an opaque copy of the lane id: in the
+    // stream-K loop the compiler would otherwise hoist them out of the loop
+    // and keep them live through the whole item, and the kernel has no
+    // registers to spare.
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     const int il = lane & 31;  // query row of this lane within each row block
     const int g = lane >> 5;   // half-wave
     const int i16 = lane & 15;
     const int half = (lane >> 4) & 1;
-
-    // Unit u = ((b*Hl + h)*n_split + split)*n_qtiles + qt: the units that run
-    // side by side on one XCD read the same keys.
-    const int unit = xcd_unit(blockIdx.x, a.n_units, a.n_xcd);
-    const int qt = unit % a.n_qtiles;
-    const int split = XS ? unit / a.n_qtiles % a.n_split : 0;
-    const int bh = XS ? unit / a.n_qtiles / a.n_split : unit / a.n_qtiles;
     const int h = bh % a.Hl;
     const int64_t b = bh / a.Hl;
     const int64_t S = a.S;
@@ -284,24 +296,11 @@ void attn_fwd(AttnArgs a)
     // [p*S/P, (p+1)*S/P) back to back), read in place.
     const int rs = a.in_heads * D;  // elements between sequence rows
     const int64_t head = (b * S * a.in_heads + a.in_head0 + h) * D;
-    // Keys of this wave's group: the KS groups split the K/V tiles evenly
-    // (KS = 2 only runs for an even tile count, so both groups run the same
-    // iterations and barriers).  In an XS launch, split s of n first takes
-    // units [s*U/n, (s+1)*U/n) of the U = tiles/KS units of KS tiles each
-    // (parts of at least 8 units), and its groups halve that run.  Every
-    // group has a full first tile.  Skv keys starting at key kvbase.
-    const int nt_all = (int)((S + KB - 1) / KB);
-    int ntiles;
-    int64_t kvbase;
-    if constexpr (XS) {
-        const int U = nt_all / KS;
-        const int u0 = (int)((int64_t)split * U / a.n_split), u1 = (int)((int64_t)(split + 1) * U / a.n_split);
-        ntiles = u1 - u0;
-        kvbase = (int64_t)(u0 * KS + grp * ntiles) * KB;
-    } else {
-        ntiles = nt_all / KS;
-        kvbase = (int64_t)grp * ntiles * KB;
-    }
+    // Keys of this wave's group: Skv keys starting at key kvbase (the KS
+    // groups of a work item run the same number of tiles, so the same
+    // iterations and barriers).
+    const int ntiles = ntl;
+    const int64_t kvbase = (int64_t)(kt0 + grp * ntl) * KB;
     const int64_t Skv = S - kvbase < (int64_t)ntiles * KB ? S - kvbase : (int64_t)ntiles * KB;
     const uint16_t *qh = a.q + head;
     const uint16_t *kh = a.k + head + kvbase * rs;
@@ -808,7 +807,7 @@ void attn_fwd(AttnArgs a)
         const int64_t sstride = (int64_t)NWG * NX * 64;  // floats per split
         float *const part0 = a.ws_part + tile * a.n_split * sstride + wq * NX * 64 + lane;
         if (grp == 0) {
-            float *const mine = part0 + split * sstride;
+            float *const mine = part0 + part * sstride;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -831,7 +830,7 @@ void attn_fwd(AttnArgs a)
         if (threadIdx.x == 0) {
             const unsigned seen = __hip_atomic_fetch_add(a.ws_cnt + tile, 1u, __ATOMIC_RELEASE,
                                                          __HIP_MEMORY_SCOPE_AGENT);
-            const int last = seen == (unsigned)(a.n_split - 1);
+            const int last = seen == (unsigned)(nparts - 1);
             if (last) {
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // every part's release is seen
                 atomicExch(a.ws_cnt + tile, 0u);
@@ -853,10 +852,10 @@ void attn_fwd(AttnArgs a)
 #pragma unroll
                 for (int db = 0; db < DB; ++db) own[db] = oacc[rb][db];
                 float M = 0.f, L = 0.f;
-                for (int i = 0; i < a.n_split; ++i) {
+                for (int i = 0; i < nparts; ++i) {
                     f32x16 oi[DB];
                     float mi, li;
-                    if (i == split) {
+                    if (i == part) {
 #pragma unroll
                         for (int db = 0; db < DB; ++db) oi[db] = own[db];
                         mi = m_run[rb];
@@ -964,6 +963,68 @@ void attn_fwd(AttnArgs a)
             t[3] = tr_c1 - tr_c0;
         }
     }
+    };
+
+    // The work of this workgroup, one call site so the body is inlined once.
+    //  * Plain builds: unit u = (b*Hl + h)*n_qtiles + qt, all keys.
+    //  * XS builds, key split: unit u = ((b*Hl + h)*n_split + split)*n_qtiles
+    //    + qt; split s of n takes units [s*U/n, (s+1)*U/n) of the U =
+    //    tiles/KS units of KS tiles each (parts of at least 8 units), and its
+    //    key groups halve that run.  The units that run side by side on one
+    //    XCD read the same keys.
+    //  * XS builds, stream-K (one key group, one row block per wave: the
+    //    two-row-block kernel has no registers to spare for the loop):
+    //    workgroup w takes iterations
+    //    [w L, (w+1) L) of the sequence of (query tile, key tile) pairs, query
+    //    tiles (bh * n_qtiles + qt) outermost, so every workgroup does the
+    //    same work, in one round; a query tile's keys are cut at the
+    //    workgroup boundaries into parts, numbered in key order.  Workgroups
+    //    with neighbouring runs (the same head) run on one XCD.
+    const int nt_all = (int)((a.S + KB - 1) / KB);  // key tiles of a query tile
+    const int wid = xcd_unit(blockIdx.x, a.n_units, a.n_xcd);
+    const bool sk = XS && KS == 1 && RB == 1 && a.sk_iters > 0;
+    const int64_t L = a.sk_iters, T = nt_all;
+    int64_t it = sk ? (int64_t)wid * L : 0;
+    const int64_t end = sk ? ((int64_t)wid + 1) * L < (int64_t)a.n_units_q * T ? ((int64_t)wid + 1) * L
+                                                                                : (int64_t)a.n_units_q * T
+                           : 0;
+    // The host launches ceil(total / L) workgroups, so every run is
+    // non-empty; a workgroup past the end would otherwise take a query tile
+    // beyond the last (and a negative tile count) in the loop below.
+    if (sk && it >= end) return;
+    do {
+        int qt, bh, kt0, ntl, part, nparts;
+        if (sk) {
+            const int64_t tile = it / T;
+            kt0 = (int)(it - tile * T);
+            ntl = (int)(T - kt0 < end - it ? T - kt0 : end - it);
+            const int first = (int)(tile * T / L), last = (int)(((tile + 1) * T - 1) / L);
+            part = wid - first;
+            nparts = last - first + 1;
+            qt = (int)(tile % a.n_qtiles);
+            bh = (int)(tile / a.n_qtiles);
+            __syncthreads();  // the LDS of the previous item is free
+            it += ntl;
+        } else if (XS) {
+            const int split = wid / a.n_qtiles % a.n_split;
+            const int U = nt_all / KS;
+            const int u0 = (int)((int64_t)split * U / a.n_split), u1 = (int)((int64_t)(split + 1) * U / a.n_split);
+            qt = wid % a.n_qtiles;
+            bh = wid / a.n_qtiles / a.n_split;
+            kt0 = u0 * KS;
+            ntl = u1 - u0;
+            part = split;
+            nparts = a.n_split;
+        } else {
+            qt = wid % a.n_qtiles;
+            bh = wid / a.n_qtiles;
+            kt0 = 0;
+            ntl = nt_all / KS;
+            part = 0;
+            nparts = 1;
+        }
+        run(wid, qt, bh, kt0, ntl, part, nparts);
+    } while (sk && it < end);
 }
 
 // Epilogue stores alone: the attention kernel's grid, work-unit order and
@@ -1177,14 +1238,34 @@ constexpr int64_t kSplitPartKeys = 128;
 
 struct SplitPlan {
     LaunchShape ls;
-    int n;
+    int n;         // parts per query tile (stream-K: the most any query tile has)
+    int sk_iters;  // stream-K: (query tile, key tile) iterations per workgroup; 0: no
 };
+
+// Stream-K candidate for a shape with one key group and one row block per
+// wave: `cus` workgroups, each on L
+// = ceil(total / cus) consecutive iterations of the (query tile, key tile)
+// sequence.  Returns L (0 when the runs would be under 16 key tiles) and the
+// most parts any query tile is cut into.
+int64_t stream_k(int64_t qtiles, int64_t T, int64_t cus, int *max_parts)
+{
+    const int64_t total = qtiles * T;
+    const int64_t L = (total + cus - 1) / cus;
+    if (L < 16) return 0;
+    int mp = 1;
+    for (int64_t t = 0; t < qtiles; ++t) {
+        const int64_t first = t * T / L, last = ((t + 1) * T - 1) / L;
+        mp = (int)(last - first + 1) > mp ? (int)(last - first + 1) : mp;
+    }
+    *max_parts = mp;
+    return L;
+}
 
 SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d, int64_t cus)
 {
     const LaunchShape plain = launch_shape(B, S, Hl, d, cus);
     const auto units = [&](const LaunchShape &ls) { return B * Hl * ((S + ls.rows() - 1) / ls.rows()); };
-    SplitPlan best = {plain, 1};
+    SplitPlan best = {plain, 1, 0};
     if (units(plain) >= kSplitMaxTiles) return best;
     const int64_t U0 = (S + plain.kb - 1) / plain.kb / plain.ks;
     int64_t best_cost = (units(plain) + cus - 1) / cus * (U0 * plain.kb + kSplitFixedKeys);
@@ -1199,10 +1280,25 @@ SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d, int64_t cus)
             const int64_t cost = (units(ls) * n + cus - 1) / cus *
                                  ((U + n - 1) / n * ls.kb + kSplitFixedKeys + kSplitPartKeys * (n - 1));
             if (cost < best_cost) {
-                best = {ls, n};
+                best = {ls, n, 0};
                 best_cost = cost;
             }
         }
+    // stream-K: one round of equal runs; each workgroup pays up to two work
+    // items' fixed cost and the merging one a round trip per other part.  It
+    // has to beat the best plan above by 3% (a full last round gains nothing)
+    for (int c = 0; c < ncand; ++c) {
+        const LaunchShape &ls = cands[c];
+        if (ls.nw != 8 || ls.ks != 1 || ls.rb != 1) continue;
+        int mp = 1;
+        const int64_t L = stream_k(units(ls), (S + ls.kb - 1) / ls.kb, cus, &mp);
+        if (L == 0 || mp < 2) continue;
+        const int64_t cost = L * ls.kb + 2 * kSplitFixedKeys + kSplitPartKeys * (mp - 1);
+        if (cost * 100 < best_cost * 97) {
+            best = {ls, mp, (int)L};
+            best_cost = cost * 100 / 97;
+        }
+    }
     if (best.n == 1) best.ls = plain;
     // every split plan has fewer than kSplitMaxTiles query tiles (the other
     // candidate has fewer tiles than the plain shape), so its counts fit
@@ -1259,6 +1355,11 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 
 int key_split(int64_t B, int64_t S, int64_t Hl, int d) { return split_plan(B, S, Hl, d, device_info().cus).n; }
 
+int64_t stream_k_iters(int64_t B, int64_t S, int64_t Hl, int d)
+{
+    return split_plan(B, S, Hl, d, device_info().cus).sk_iters;
+}
+
 int64_t workspace_count_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 {
     const SplitPlan sp = split_plan(B, S, Hl, d, device_info().cus);
@@ -1270,7 +1371,7 @@ int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
     const SplitPlan sp = split_plan(B, S, Hl, d, device_info().cus);
     if (sp.n == 1) return 0;
     const int64_t tiles = B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows());
-    return kCountBytes + tiles * sp.n * part_floats_per_split(sp.ls, d) * 4;
+    return kCountBytes + tiles * sp.n * part_floats_per_split(sp.ls, d) * 4;  // n parts' slots per query tile
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -1280,7 +1381,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
 {
     const DeviceInfo dv = device_info();
     const SplitPlan sp = workspace && !trace ? split_plan(B, S, Hl, d, dv.cus)
-                                             : SplitPlan{launch_shape(B, S, Hl, d, dv.cus), 1};
+                                             : SplitPlan{launch_shape(B, S, Hl, d, dv.cus), 1, 0};
     const LaunchShape ls = sp.ls;
     const int n_split = sp.n;
     AttnArgs a;
@@ -1301,10 +1402,15 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.ws_cnt = nullptr;
     a.ws_part = nullptr;
     const void *fn;
+    a.sk_iters = sp.sk_iters;
+    a.n_units_q = a.n_units;
     if (n_split > 1) {
         a.ws_cnt = (unsigned *)workspace;
         a.ws_part = (float *)((char *)workspace + kCountBytes);
-        a.n_units *= n_split;
+        // stream-K: one workgroup per run of sk_iters iterations (at most one
+        // per CU; the last run may be shorter); else n_split per query tile
+        const int64_t total = (int64_t)a.n_units * ((S + ls.kb - 1) / ls.kb);
+        a.n_units = sp.sk_iters > 0 ? (int32_t)((total + sp.sk_iters - 1) / sp.sk_iters) : a.n_units * n_split;
         fn = attention_kernel_xs(d, ls);
     } else {
         fn = trace ? attention_kernel<true>(d, ls) : attention_kernel<false>(d, ls);

@@ -187,8 +187,18 @@ size_t ua_workspace_bytes(const ua_shape *shp, int P);
  * shape that splits, 0 when the shape needs no workspace. */
 size_t ua_workspace_count_bytes(const ua_shape *shp, int P);
 /* Workgroups sharing each query tile's keys in a *_ws call (1: no split; 0
- * for an invalid or empty shape). */
+ * for an invalid or empty shape).  For a stream-K split (below) the most
+ * parts any query tile is cut into. */
 int ua_key_split(const ua_shape *shp, int P);
+/* The *_ws calls split a query tile's keys in one of two ways.  Either each
+ * query tile's keys go to ua_key_split workgroups in equal runs, or, when
+ * that leaves CUs idle in a last round, stream-K: one workgroup per CU, each
+ * taking an equal run of ua_stream_k_iters consecutive (query tile, key tile)
+ * iterations across query-tile boundaries, in one round; a query tile's keys
+ * are then cut at the workgroup boundaries into at most ua_key_split parts.
+ * Returns that run length for a stream-K split, else 0 (also for an invalid
+ * or empty shape). */
+int64_t ua_stream_k_iters(const ua_shape *shp, int P);
 
 /*
  * Both exchanges fused.  Fig. 5 steps (a)-(c) of the review page: the

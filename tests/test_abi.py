@@ -208,11 +208,13 @@ def test_key_split_choice_and_workspace_size():
     assert ua.key_split(2, 32768, 24, 64, 4) == 1 and ua.workspace_bytes(2, 32768, 24, 64, 4) == 0
     assert ua.key_split(1, 512, 4, 64, 2) == 1 and ua.workspace_bytes(1, 512, 4, 64, 2) == 0
     nx = 4 * 16 + 2                                 # floats per lane at d = 128: O^T blocks, m, l
-    # dit_long: 192 tiles of 256 rows over 256 key tiles of 64: n = 4 gives
-    # 768 workgroups = 3 rounds of 64 tiles: 3 * (4096 + 512 + 384) against
-    # 1 * (16384 + 512) and 2 * (8192 + 640)
-    assert ua.key_split(1, 16384, 24, 128, 8) == 4
-    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 4096 + 192 * 4 * 8 * nx * 64 * 4
+    # dit_long: 192 tiles of 256 rows over 256 key tiles of 64.  The best
+    # plain key split, n = 4 (768 workgroups = 3 rounds of 64 tiles: 3 *
+    # (4096 + 512 + 384) = 14976), loses to stream-K: 256 workgroups of
+    # 49152 / 256 = 192 iterations, L * 64 + 2 * 512 + 128 * (2 - 1) = 13440,
+    # every query tile cut into at most 2 parts
+    assert ua.key_split(1, 16384, 24, 128, 8) == 2 and ua.stream_k_iters(1, 16384, 24, 128, 8) == 192
+    assert ua.workspace_bytes(1, 16384, 24, 128, 8) == 4096 + 192 * 2 * 8 * nx * 64 * 4
     # dit_image: 96 tiles of 128 rows (two key groups of 4 waves on 32-key
     # tiles): n = 2 (1024 + 640) beats n = 1 (2048 + 512), and the 256-row
     # shape on 64-key tiles split 4 ways (1024 + 896)
@@ -232,11 +234,14 @@ def test_key_split_choice_and_workspace_size():
     # 32-key tiles per workgroup (4 storing waves per workgroup)
     assert ua.key_split(1, 4096, 8, 128, 8) == 4
     assert ua.workspace_bytes(1, 4096, 8, 128, 8) == 4096 + 32 * 4 * 4 * nx * 64 * 4
-    # 320 tiles (1.25 rounds) of video_dit's heads at 16384 keys: n = 4, five
-    # full rounds of 64 key tiles (5 * 4992) against 2 * 16896; at 32768 keys
-    # 640 tiles (2.5 rounds) split 2 ways
-    assert ua.key_split(1, 16384, 40, 128, 8) == 4
-    assert ua.key_split(1, 32768, 40, 128, 8) == 2
+    # 320 tiles (1.25 rounds) of video_dit's heads at 16384 keys: the best
+    # plain split, n = 4 (five full rounds of 64 key tiles, 5 * 4992 = 24960),
+    # loses to stream-K (320 iterations per workgroup: 20480 + 1024 + 128);
+    # at 32768 keys 640 tiles (2.5 rounds) split 2 ways (five full rounds),
+    # which stream-K does not beat by the 3% it must
+    assert ua.key_split(1, 16384, 40, 128, 8) == 2 and ua.stream_k_iters(1, 16384, 40, 128, 8) == 320
+    assert ua.workspace_bytes(1, 16384, 40, 128, 8) == 4096 + 320 * 2 * 8 * nx * 64 * 4
+    assert ua.key_split(1, 32768, 40, 128, 8) == 2 and ua.stream_k_iters(1, 32768, 40, 128, 8) == 0
     assert ua.workspace_bytes(1, 32768, 40, 128, 8) == 4096 + 640 * 2 * 8 * nx * 64 * 4
     # an odd 32-key tile count puts the plain call on one wave per SIMD (4-wave
     # workgroups of 128 rows); the split runs the 8-wave 256-row shape instead:
@@ -274,11 +279,11 @@ def test_noalloc_validates_and_rejects_splits_beyond_its_scratch():
     assert call((1, 4096, 24, 128), q=0) == ua.UA_ERR_NULL
     assert call((1, 4096, 24, 128), out=O + 2) == ua.UA_ERR_ALIGN
     assert call((0, 4096, 24, 128), q=0, k=0, v=0, out=0) == ua.UA_OK    # empty: nothing touched
-    # the heads of the video workload at 16384 keys split 4 ways over 320
-    # query tiles: ~165 MiB of partials, beyond the 128 MiB scratch
-    need = ua.workspace_bytes(1, 16384, 40, 128, 8)
+    # the heads of the video workload at 32768 keys (640 query tiles split
+    # 2 ways): ~165 MiB of partials, beyond the 128 MiB scratch
+    need = ua.workspace_bytes(1, 32768, 40, 128, 8)
     assert need > ua.SCRATCH_BYTES == 128 << 20
-    assert call((1, 16384, 40, 128)) == ua.UA_ERR_SCRATCH
+    assert call((1, 32768, 40, 128)) == ua.UA_ERR_SCRATCH
     assert "scratch" in ua.status_string(ua.UA_ERR_SCRATCH)
     text = open(HEADER).read()
     assert re.search(r"#define\s+UA_SCRATCH_BYTES\s+\(\(size_t\)128 << 20\)", text)

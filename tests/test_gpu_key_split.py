@@ -72,7 +72,7 @@ SPLIT_CASES = [
     (1, 16384, 48, 8, 1, 64, 45, 4),   # d = 64, two row blocks per wave
     (1, 3584, 8, 8, 1, 64, 51, 4),     # d = 64 with key groups, parts of 14 tile pairs
     (1, 4064, 8, 8, 6, 128, 52, 4),    # plain call on one wave per SIMD; split on the 8-wave shape, ragged last key tile
-    (1, 16384, 40, 8, 7, 128, 54, 4),  # 320 tiles (1.25 rounds unsplit): five full rounds
+    (1, 16384, 40, 8, 7, 128, 54, 2),  # 320 tiles (1.25 rounds unsplit): stream-K, 320 iterations per workgroup
     (1, 32768, 40, 8, 2, 128, 55, 2),  # 640 tiles (2.5 rounds unsplit): five full rounds
 ]
 

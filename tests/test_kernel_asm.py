@@ -263,8 +263,11 @@ def test_split_partials_complete_before_the_barrier(asm):
         stores = [i for i, l in enumerate(lines) if _is_sc1_store(l)]
         adds = [i for i, l in enumerate(lines) if l.startswith("global_atomic_add")]
         assert stores and adds, name
-        # the check is not vacuous: a barrier lies between the partial stores and the add
-        assert any(l == "s_barrier" for l in lines[stores[-1]:adds[0]]), name
+        # the check is not vacuous: between every arrival add and the partial
+        # stores laid out before it lies a barrier
+        for ad in adds:
+            before = [i for i in stores if i < ad]
+            assert before and any(l == "s_barrier" for l in lines[before[-1]:ad]), name
         bad = barriers_with_stores_in_flight(lines)
         assert not bad, "%s: %s" % (name, bad[:3])
 

@@ -80,3 +80,84 @@ def test_split_covers_every_key_tile_once_and_stays_in_the_workspace(B, S, H, d,
     assert np.all(covered == 1)                  # every key tile exactly once per query tile
     assert tiles < 1024 and cnt_bytes >= tiles * 4  # one count per query tile
     assert cnt_bytes + (max_part + 1) * 4 == total
+
+
+# ---- stream-K: the workgroups' runs, restated from the kernel and launch ----
+
+def _sk_shapes():
+    """Shapes whose *_ws calls run stream-K: the DiT-long workload, the GPU
+    tests' cases, and a scan of lengths, head counts, batches and head dims."""
+    out = {(1, 16384, 24, 128, 8), (1, 16384, 40, 128, 8), (2, 3000, 48, 64, 8), (1, 5000, 64, 64, 8),
+           (1, 12344, 24, 128, 8)}
+    for d in (64, 128):
+        for S in (2000, 3000, 4104, 5000, 6000, 8000, 9999, 12000, 16000, 20000):
+            for Hl in (1, 2, 3, 5, 6, 8):
+                for B in (1, 2):
+                    if ua.stream_k_iters(B, S, Hl * 8, d, 8):
+                        out.add((B, S, Hl * 8, d, 8))
+    return sorted(out)
+
+
+SK_SHAPES = _sk_shapes()
+
+
+def sk_items(qtiles, T, L, launched, guard=True):
+    """The work items of every launched workgroup, as the kernel forms them:
+    (workgroup, query tile, first key tile, key tiles, part, parts)."""
+    total = qtiles * T
+    items = []
+    for w in range(launched):
+        it, end = w * L, min((w + 1) * L, total)
+        if guard and it >= end:
+            continue
+        while True:
+            tile = it // T
+            k0 = it - tile * T
+            n = min(T - k0, end - it)
+            first, last = tile * T // L, ((tile + 1) * T - 1) // L
+            items.append((w, tile, k0, n, w - first, last - first + 1))
+            it += n
+            if not it < end:
+                break
+    return items
+
+
+@pytest.mark.parametrize("B,S,H,d,P", SK_SHAPES)
+def test_stream_k_runs_cover_every_iteration_once(B, S, H, d, P):
+    Hl = H // P
+    L = ua.stream_k_iters(B, S, H, d, P)
+    n = ua.key_split(B, S, H, d, P)
+    assert L >= 16 and n >= 2
+    rows, kb = 256, 64                      # stream-K runs the 8-wave 256-row shape on 64-key tiles
+    qtiles, T = B * Hl * -(-S // rows), -(-S // kb)
+    assert qtiles < 1024                    # arrival counts fit the fixed count region
+    nx = (d // 32) * 16 + 2
+    assert ua.workspace_bytes(B, S, H, d, P) == 4096 + qtiles * n * 8 * nx * 64 * 4
+    launched = -(-(qtiles * T) // L)        # the launch: ceil(total / L) workgroups
+    assert launched <= 256
+    items = sk_items(qtiles, T, L, launched)
+    covered = np.zeros((qtiles, T), np.int64)
+    parts = {}
+    for w, tile, k0, m, part, nparts in items:
+        assert 0 <= tile < qtiles and 0 <= k0 < T and 1 <= m <= T - k0
+        assert 0 <= part < nparts <= n      # partial slots (tile * n + part) inside the workspace
+        covered[tile, k0:k0 + m] += 1
+        parts.setdefault(tile, []).append((part, nparts, k0))
+    assert np.all(covered == 1)
+    for tile, ps in parts.items():
+        # parts numbered 0 .. nparts-1 in key order, each exactly once
+        ps.sort(key=lambda p: p[2])
+        assert [p[0] for p in ps] == list(range(len(ps))) and all(p[1] == len(ps) for p in ps)
+    assert max(len(ps) for ps in parts.values()) == n
+
+
+def test_stream_k_without_the_launch_count_and_guard_runs_out_of_range():
+    # One workgroup per CU and no guard: for B=2, S=3000, 48 heads over 8
+    # ranks, d=64, 256 * 27 iterations exceed the 6768 there are, and the
+    # workgroups past the end take query tile 144 of 144 with a negative tile
+    # count -- the out-of-range reads this layout guards against.
+    L = ua.stream_k_iters(2, 3000, 48, 64, 8)
+    qtiles, T = 2 * 6 * 12, 47
+    assert L == 27 and 256 * L > qtiles * T
+    bad = [it for it in sk_items(qtiles, T, L, 256, guard=False) if it[1] >= qtiles or it[3] < 1]
+    assert bad and bad[0][1] == qtiles and bad[0][3] < 0
