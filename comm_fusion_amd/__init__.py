@@ -29,6 +29,7 @@ the MoE expert path with the Combine fused into Linear-2 (include/moe_combine.h)
 and, for measurement only,
   attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None)
   epilogue_store_only(B, S, H, d, rank, P, out, stream=None)
+  fused_write_counts(Q, K, V, rank, P, out, counts, workspace=None, scale=None, stream=None)
   work_units(B, S, H, d, P)
 Tensors are torch tensors on the GPU: Q, K, V, O_local bfloat16
 [B][S][Hl][d]; out bfloat16 with B*S*(Hl*P)*d elements, laid out
@@ -41,7 +42,7 @@ from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # no
                        a2a_gather, a2a_permute, attn_serial, attn_serial_ws, attn_ulysses_fused,
                        attn_ulysses_fused_io, attn_ulysses_fused_io_ws, attn_ulysses_fused_trace,
                        attn_ulysses_fused_noalloc, attn_ulysses_fused_ws,
-                       dest_bytes, epilogue_store_only, key_split, lib, lib_path, local_bytes,
+                       dest_bytes, epilogue_store_only, fused_write_counts, key_split, lib, lib_path, local_bytes,
                        new_workspace, status_string, stream_k_iters, version, work_units, workspace_bytes,
                        workspace_count_bytes)
 from ._moe_binding import (MOE_EXPERT_WAVE, MOE_INTERLEAVED, MOE_MAX_WAVE, MoeShape,  # noqa: F401,E402

@@ -361,3 +361,28 @@ def attn_ulysses_fused_noalloc(Q, K, V, rank, P, out, scale=None, stream=None):
                                           ctypes.byref(shp), scale, _stream(stream, Q, K, V, out))
     if st != UA_OK:
         raise UAError("attn_ulysses_fused_noalloc", st)
+
+
+def fused_write_counts(Q, K, V, rank, P, out, counts, workspace=None, scale=None, stream=None):
+    """Write check: attn_ulysses_fused_ws (or the plain call) that also adds 1
+    to counts[c] (int32 tensor of out.numel() // 8 entries, zeroed) for every
+    16-byte chunk c of out it stores."""
+    import torch
+    shp = _qkv_shape(Q, K, V, P)
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_bf16(n, t)
+    _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
+    if counts.dtype != torch.int32 or not counts.is_cuda or counts.numel() != out.numel() // 8:
+        raise TypeError("counts must be an int32 GPU tensor of out.numel() // 8 elements")
+    wp, wb = _ws(workspace)
+    scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
+    L = lib()
+    L.ua_fused_write_counts.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                                  ctypes.POINTER(Shape), ctypes.c_float,
+                                                                  ctypes.c_void_p, ctypes.c_size_t,
+                                                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.ua_fused_write_counts.restype = ctypes.c_int
+    st = L.ua_fused_write_counts(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out), ctypes.byref(shp),
+                                 scale, wp, wb, _stream(stream, Q, K, V, out, counts), _ptr(counts))
+    if st != UA_OK:
+        raise UAError("ua_fused_write_counts", st)

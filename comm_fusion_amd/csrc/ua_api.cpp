@@ -97,7 +97,7 @@ ua::Placement local_placement(void *o_local, const ua_shape *shp, int P)
 int attention_call(const void *Q, const void *K, const void *V, int rank, int P, void *out,
                    const ua_shape *shp, float scale, hipStream_t stream, bool fused, uint64_t *trace = nullptr,
                    bool want_trace = false, bool seq_input = false, bool want_ws = false,
-                   void *ws = nullptr, size_t ws_bytes = 0)
+                   void *ws = nullptr, size_t ws_bytes = 0, uint32_t *wcount = nullptr, bool want_count = false)
 {
     int64_t elems = 0;
     int st = check_shape(shp, rank, P, &elems);
@@ -106,8 +106,9 @@ int attention_call(const void *Q, const void *K, const void *V, int rank, int P,
     if ((st = check_limits(shp, P)) != UA_OK) return st;
     if (seq_input && (st = check_limits_seq(shp)) != UA_OK) return st;
     if (empty(shp)) return UA_OK;
-    if (!Q || !K || !V || !out || (want_trace && !trace)) return UA_ERR_NULL;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || (want_trace && !aligned16(trace)))
+    if (!Q || !K || !V || !out || (want_trace && !trace) || (want_count && !wcount)) return UA_ERR_NULL;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || (want_trace && !aligned16(trace)) ||
+        (want_count && !aligned16(wcount)))
         return UA_ERR_ALIGN;
     const int64_t Hl = shp->H / P;
     const int64_t need = want_ws ? ua::workspace_bytes(shp->B, shp->S, Hl, (int)shp->d) : 0;
@@ -122,7 +123,7 @@ int attention_call(const void *Q, const void *K, const void *V, int rank, int P,
     const hipError_t e = ua::launch_attention((const uint16_t *)Q, (const uint16_t *)K,
                                               (const uint16_t *)V, in_heads, in_head0, shp->B, shp->S,
                                               Hl, (int)shp->d, scale, o, (hipStream_t)stream, trace,
-                                              need > 0 ? ws : nullptr);
+                                              need > 0 ? ws : nullptr, (unsigned *)wcount);
     return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
@@ -237,6 +238,14 @@ int a2a_gather(const void *X, int rank, int P, void *X_local, const ua_shape *sh
     const hipError_t e = ua::launch_gather(in, shp->B, shp->S, shp->H / P, (int)shp->d,
                                            (uint16_t *)X_local, (hipStream_t)stream);
     return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+int ua_fused_write_counts(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                          const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream, uint32_t *counts)
+{
+    return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, nullptr, false, false, true, workspace,
+                          workspace_bytes, counts, true);
 }
 
 int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int rank, int P, void *out,

@@ -30,11 +30,12 @@ struct Placement {
 // With a non-null trace, the measurement build runs and fills 4 uint64 per unit.
 // With a non-null workspace (workspace_bytes of the shape, counts zero on
 // entry and again on exit) and no trace, the launch splits each query tile's
-// keys over key_split workgroups.
+// keys over key_split workgroups.  With a non-null wcount, the epilogue adds
+// 1 to wcount[c] for every 16-byte chunk c (from out.base) it stores.
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t in_heads, int64_t in_head0, int64_t B, int64_t S, int64_t Hl,
                             int d, float scale, const Placement &out, hipStream_t stream,
-                            uint64_t *trace = nullptr, void *workspace = nullptr);
+                            uint64_t *trace = nullptr, void *workspace = nullptr, unsigned *wcount = nullptr);
 
 // The attention kernel's epilogue stores alone (closed-form values).
 hipError_t launch_epilogue_only(int64_t B, int64_t S, int64_t Hl, int d, const Placement &out,

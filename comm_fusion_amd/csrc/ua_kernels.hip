@@ -96,6 +96,9 @@ struct AttnArgs {
     int32_t n_xcd;     // XCDs of the device (workgroups are dealt round robin over them)
     float scale_log2;  // softmax scale * log2(e)
     uint64_t *trace;   // measurement build only: 4 timestamps per work unit
+    // write check (optional, any build): +1 per 16-byte chunk of the
+    // destination the epilogue stores, indexed from out.base
+    unsigned *wcount;
     // key split across workgroups (XS builds only): n_split workgroups per
     // query tile, each on a run of about 1/n_split of the keys; their partial
     // results meet in ws_part, and ws_cnt counts arrivals per query tile
@@ -947,6 +950,7 @@ void attn_fwd(AttnArgs a)
                 const uint32_t i = (uint32_t)sq - p * rr;
                 uint16_t *dst = o.base + (((b * o.regions + p) * o.region_rows + i) * o.heads + o.head0 + h) * D;
                 *(u32x4 *)(dst + chunk * 8) = val;
+                if (a.wcount) atomicAdd(a.wcount + (dst + chunk * 8 - o.base) / 8, 1u);
             }
         }
     }
@@ -1377,7 +1381,7 @@ int64_t workspace_bytes(int64_t B, int64_t S, int64_t Hl, int d)
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int64_t in_heads, int64_t in_head0, int64_t B, int64_t S, int64_t Hl,
                             int d, float scale, const Placement &out, hipStream_t stream,
-                            uint64_t *trace, void *workspace)
+                            uint64_t *trace, void *workspace, unsigned *wcount)
 {
     const DeviceInfo dv = device_info();
     const SplitPlan sp = workspace && !trace ? split_plan(B, S, Hl, d, dv.cus)
@@ -1398,6 +1402,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
     a.n_xcd = dv.xcds;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.trace = trace;
+    a.wcount = wcount;
     a.n_split = n_split;
     a.ws_cnt = nullptr;
     a.ws_part = nullptr;

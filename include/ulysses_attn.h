@@ -239,6 +239,21 @@ int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int ra
                              uint64_t *trace);
 
 /*
+ * Write check of the fused path ("every destination element is written
+ * exactly once"): attn_ulysses_fused_ws (the key split, stream-K, or the
+ * plain call where the shape needs no workspace) that also adds 1 to
+ * counts[c] for every 16-byte chunk c of `out` its epilogue stores (device
+ * atomics; the stores themselves are the product call's, bit for bit).
+ *   counts: device buffer of ua_dest_bytes(shp) / 16 uint32, 16-byte
+ *     aligned, owned and zeroed by the caller; NULL gives UA_ERR_NULL.
+ * After a call every chunk of this rank's head slots holds 1 and every other
+ * chunk 0.  Other arguments and errors as attn_ulysses_fused_ws.
+ */
+int ua_fused_write_counts(const void *Q, const void *K, const void *V, int rank, int P,
+                          void *out, const ua_shape *shp, float scale, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream, uint32_t *counts);
+
+/*
  * Epilogue stores alone, for measuring what the destination layout sustains:
  * the fused call's grid, work-unit order and per-lane store pattern, writing
  * a closed-form value instead of attention output.  Element (s, global head

@@ -287,3 +287,21 @@ def test_noalloc_validates_and_rejects_splits_beyond_its_scratch():
     assert "scratch" in ua.status_string(ua.UA_ERR_SCRATCH)
     text = open(HEADER).read()
     assert re.search(r"#define\s+UA_SCRATCH_BYTES\s+\(\(size_t\)128 << 20\)", text)
+
+
+def test_write_counts_validates_its_counter_buffer():
+    L = ua.lib()
+
+    def call(shape=(1, 4096, 24, 128), rank=0, P=8, counts=O + 4096, out=O, q=A, ws=None, ws_bytes=0):
+        return L.ua_fused_write_counts(q, B_, C, rank, P, out, ctypes.byref(Shape(*shape)), ctypes.c_float(0.125),
+                                       ws, ctypes.c_size_t(ws_bytes), None, counts)
+
+    assert call(counts=0) == ua.UA_ERR_NULL
+    assert call(counts=O + 4100) == ua.UA_ERR_ALIGN
+    assert call(q=0) == ua.UA_ERR_NULL
+    assert call(rank=8) == ua.UA_ERR_RANK
+    assert call((1, 4096, 24, 96)) == ua.UA_ERR_UNSUPPORTED
+    # a shape whose plan splits keys needs its workspace
+    assert ua.key_split(1, 16384, 40, 128, 8) > 1
+    assert call((1, 16384, 40, 128)) == ua.UA_ERR_NULL
+    assert call((1, 16384, 40, 128), ws=A + 8192, ws_bytes=64) == ua.UA_ERR_WORKSPACE
