@@ -432,6 +432,23 @@ void attn_fwd(AttnArgs a)
             });
         });
     };
+    // Score block jb of S^T for K tile t, read straight from global memory
+    // (the tile's LDS buffer is reused by then): the same fragments and the
+    // same MFMA order as qk, so the same values.  Full tiles only.
+    auto qk_global = [&](int t, int jb, f32x16 (&s)[RB]) {
+        const uint16_t *kr = kh + (int64_t)(t * KB + jb * 32 + il) * rs + 8 * g;
+        const f32x16 zero = {};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb] = zero;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const u32x4 kf = *(const u32x4 *)(kr + 16 * kk);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                                __builtin_bit_cast(bf16x8, qf[rb][kk]), s[rb], 0, 0, 0);
+        }
+    };
     // O^T += V^T P^T for the V tile in buffer vbuf (outside the steady loop).
     auto pv = [&](int vbuf, const u32x4 (&pb)[RB][2 * KNB]) {
         const unsigned vo = vbuf * TILE;
@@ -456,12 +473,17 @@ void attn_fwd(AttnArgs a)
         });
     };
 
-    // ---- online softmax in the log2 domain, per row block.  m_run is the
-    // running max of this row's scaled scores.  It is only a stabiliser: it
-    // is raised when a tile's max exceeds it by more than 8 (a factor 256), so
-    // P stays below 2^8 and O rarely needs rescaling; O / l comes out the same
-    // for any choice of it.  l_run is this lane's part of the row sum, taken
-    // over the same bf16-rounded P that feeds the PV product.
+    // ---- online softmax in the log2 domain, per row block.  m_run is a
+    // stabiliser, not the exact running max: O / l comes out the same for
+    // any choice of it, and fp32 has room to spare, so it is raised only
+    // when P would grow large.  The first and the last tile of a work item
+    // take their tile max first and raise m_run when it exceeds m_run by
+    // more than 8 (a factor 256).  The tiles between take P against m_run
+    // as it stands and go to an exact path only when a lane's sum of the
+    // tile's P passes 2^15 (or is +inf), where m_run is raised to the tile
+    // max; so P stays below 2^15 and O rarely needs rescaling.  l_run is
+    // this lane's part of the row sum, taken over the same bf16-rounded P
+    // that feeds the PV product.
     const float c = a.scale_log2;
     float m_run[RB], l_run[RB];
 #pragma unroll
@@ -510,9 +532,10 @@ void attn_fwd(AttnArgs a)
     // P for two neighbouring keys of chunk cc of row block rb, rounded to
     // bf16 and packed as the B operand of the PV product; the row sum takes
     // the rounded values.
-    auto exp_pair = [&](const f32x16 (&s)[RB][KNB], u32x4 (&pb)[RB][2 * KNB], int rb, int cc, int e2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][cc >> 1][8 * (cc & 1) + 2 * e2], c, -m_run[rb]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][cc >> 1][8 * (cc & 1) + 2 * e2 + 1], c, -m_run[rb]));
+    // (sb: score block cc/2 of row block rb)
+    auto exp_pair_b = [&](const f32x16 &sb, u32x4 (&pb)[RB][2 * KNB], int rb, int cc, int e2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sb[8 * (cc & 1) + 2 * e2], c, -m_run[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sb[8 * (cc & 1) + 2 * e2 + 1], c, -m_run[rb]));
         f32x2 f = {p0, p1};
         const bf16x2 hb = __builtin_convertvector(f, bf16x2);
         pb[rb][cc][e2] = __builtin_bit_cast(unsigned, hb);
@@ -521,6 +544,9 @@ void attn_fwd(AttnArgs a)
         // sinks the whole exp work towards its first use (the next
         // iteration's PV MFMAs) and runs it as one block without MFMA overlap.
         asm volatile("" : "+v"(pb[rb][cc][e2]), "+v"(l_run[rb]));
+    };
+    auto exp_pair = [&](const f32x16 (&s)[RB][KNB], u32x4 (&pb)[RB][2 * KNB], int rb, int cc, int e2) {
+        exp_pair_b(s[rb][cc >> 1], pb, rb, cc, e2);
     };
     auto softmax_exp = [&](const f32x16 (&s)[RB][KNB], u32x4 (&pb)[RB][2 * KNB]) {
 #pragma unroll
@@ -566,16 +592,18 @@ void attn_fwd(AttnArgs a)
     // slice of the softmax VALU work, and scheduling fences keep the
     // compiler from gathering it into one block.
     //   Fragment order: PV_{t-1} (chunk cc, block db), then S_{t+1} (block
-    //   jb, k-step kk).  VALU order: tile max of S_t in NMX slots, then the
-    //   raise step, then EPS exp pairs per slot.
+    //   jb, k-step kk).  VALU work: the exp pairs of S_t, taken against the
+    //   running max as it stands (no tile max in the loop), from the first
+    //   slot on.  The tile's lane sums are checked at the start of the next
+    //   iteration, after the barrier and before PV uses that P; the exact
+    //   path (rare) forms the tile's S again from K in global memory, takes
+    //   its max, raises m_run to it and forms P again.
     constexpr int NPV = 2 * KNB * DB;  // PV fragments
     constexpr int NS = KNB * KK;       // S fragments
     constexpr int NF = NPV + NS;       // fragments per iteration
     constexpr int NM = NF * RB;        // MFMAs (slots) per iteration
-    constexpr int NMX = 2 * KNB * RB;  // max slots, 8 values each
     constexpr int NEX = 8 * KNB * RB;  // exp pairs
-    constexpr int EPS = (NEX + (NM - NMX - 1) - 1) / (NM - NMX - 1);
-    static_assert(NM > NMX + 1, "no slots left for the exp pairs");
+    constexpr int EPS = (NEX + NM - 1) / NM;  // exp pairs per slot
     static_assert(kPF <= NPV, "the prefetch crossing into the next iteration reads V fragments");
     constexpr int NRD_PV = 2, NRD_S = 1;  // LDS reads per fragment
     // reads issued after fragment f's and before its first MFMA (fragments
@@ -606,6 +634,53 @@ void attn_fwd(AttnArgs a)
     constexpr int FR = 4;
     static_assert(FR > kPF && NF % FR == 0 && FR == 4, "fragment ring");
     u32x4 fr[FR] = {};
+    // Row sums before the last tile's P was added (for its sum check).
+    float l_chk[RB];
+    // Sum check of tile u, whose P sits in p_prv: a lane sum of its P above
+    // 2^15 (also +inf) sends it to the exact path, which restores the row
+    // sums, forms S_u again from K_u in global memory, takes its max, raises
+    // m_run to it when it exceeds m_run by more than 8 (always, as a sum
+    // above 2^15 of at most 32 values needs one above 2^10; rescaling O, which
+    // holds PV up to u-1) and forms P_u again.  u < ntiles - 1 (full tiles).
+    auto check_prev = [&](int u) {
+        bool big = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) big |= l_run[rb] - l_chk[rb] > 32768.0f;
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(big) == 0, 1)) return;
+        float mt[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) mt[rb] = -INFINITY;
+#pragma unroll
+        for (int jb = 0; jb < KNB; ++jb) {
+            f32x16 s_re[RB];
+            qk_global(u, jb, s_re);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt[rb] = fmaxf(mt[rb], s_re[rb][r]);
+        }
+        float alpha[RB];
+        bool raised = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            l_run[rb] = l_chk[rb];
+            raised |= raise_max(rb, row_max(mt[rb]) * c, alpha[rb]);
+        }
+        // P in the order of softmax_exp (row block, chunk, pair)
+        static_assert(RB == 1 || KNB == 1, "one score block at a time keeps that order");
+#pragma unroll
+        for (int jb = 0; jb < KNB; ++jb) {
+            f32x16 s_re[RB];
+            qk_global(u, jb, s_re);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int cc = 2 * jb; cc < 2 * jb + 2; ++cc)
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) exp_pair_b(s_re[rb], p_prv, rb, cc, e2);
+        }
+        if (__builtin_amdgcn_ballot_w64(raised) != 0) rescale_o(alpha);
+    };
     auto steady = [&](int t, auto par) {
         constexpr int P = decltype(par)::value;  // t % 3
         using VB = std::integral_constant<int, (P + 2) % 3>;   // V_{t-1}
@@ -616,11 +691,11 @@ void attn_fwd(AttnArgs a)
         // every wave is done with iteration t-1: K_t's and V_{t-2}'s buffers
         // are free for K_{t+3} and V_{t+1}.
         sync_tiles();
+        check_prev(t - 1);
         if (t + 3 < ntiles) copy_k(t + 3, P);
         copy_v(t + 1, (P + 1) % 3);
-        float mx[NMX];
-        float alpha[RB];
-        bool any = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) l_chk[rb] = l_run[rb];
         static_for<NM>([&](auto mc) {
             constexpr int m = decltype(mc)::value;
             constexpr int f = m / RB, r = m % RB;  // fragment, row block
@@ -647,40 +722,16 @@ void attn_fwd(AttnArgs a)
                         __builtin_bit_cast(bf16x8, fg), __builtin_bit_cast(bf16x8, qf[r][kk]), s_nxt[r][jb], 0, 0, 0);
                 }
             }
-            // softmax slice of slot m
-            if constexpr (m < NMX) {
-                // one running max per row block, two new values per v_max3
-                constexpr int mrb = m / (2 * KNB), ms = m % (2 * KNB);
-                constexpr int jb = ms >> 1, r0 = (ms & 1) * 8;
-                float v;
-                if constexpr (ms == 0)
-                    v = fmaxf(fmaxf(s_cur[mrb][jb][0], s_cur[mrb][jb][1]), s_cur[mrb][jb][2]);
-                else
-                    v = fmaxf(fmaxf(mx[m - 1], s_cur[mrb][jb][r0]), s_cur[mrb][jb][r0 + 1]);
-                constexpr int i0 = ms == 0 ? 3 : 2;
-#pragma unroll
-                for (int i = i0; i + 1 < 8; i += 2) v = fmaxf(fmaxf(v, s_cur[mrb][jb][r0 + i]), s_cur[mrb][jb][r0 + i + 1]);
-                if constexpr (i0 == 3) v = fmaxf(v, s_cur[mrb][jb][r0 + 7]);
-                mx[m] = v;
-                asm volatile("" : "+v"(mx[m]));
-            } else if constexpr (m == NMX) {
-                bool raised = false;
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    raised |= raise_max(rb, row_max(mx[(rb + 1) * 2 * KNB - 1]) * c, alpha[rb]);
-                any = __builtin_amdgcn_ballot_w64(raised) != 0;
-            } else {
-                static_for<EPS>([&](auto xc) {
-                    constexpr int e = (m - NMX - 1) * EPS + decltype(xc)::value;
-                    if constexpr (e < NEX) {
-                        constexpr int erb = e / (8 * KNB), w = e % (8 * KNB);
-                        exp_pair(s_cur, p_cur, erb, w >> 2, w & 3);
-                    }
-                });
-            }
+            // softmax slice of slot m: exp pairs m*EPS .. m*EPS+EPS-1
+            static_for<NEX>([&](auto ec) {
+                constexpr int e = decltype(ec)::value;
+                if constexpr (e / EPS == m) {
+                    constexpr int erb = e / (8 * KNB), w = e % (8 * KNB);
+                    exp_pair(s_cur, p_cur, erb, w >> 2, w & 3);
+                }
+            });
             __builtin_amdgcn_sched_barrier(0);
         });
-        if (any) rescale_o(alpha);
         rotate();
     };
     // Full wait (also drains operand reads still in flight) and barrier.
@@ -706,6 +757,8 @@ void attn_fwd(AttnArgs a)
     } else {
         qk(1, s_nxt);
         softmax_exp(s_cur, p_cur);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) l_chk[rb] = l_run[rb];
         rotate();
         // every wave is done with K_0: its buffer takes K_3; V_1 goes to buffer 1
         sync_all();
@@ -741,6 +794,7 @@ void attn_fwd(AttnArgs a)
         // registers stay reserved (tied to this wait) until they land.
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fr[0]), "+v"(fr[1]), "+v"(fr[2]), "+v"(fr[3])::"memory");
         sync_all();
+        check_prev(t - 1);
         float alpha[RB];
         const bool any = softmax_max(s_cur, valid_last, alpha);
         pv((t + 2) % 3, p_prv);
