@@ -631,7 +631,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "S": w.S, "H": w.H, "P": w.P, "rank": w.rank,
                    "d": w.d, "Hl": w.Hl, "flops_per_step": w.flops, "causal": False,
-                   "key_split": n_split},
+                   "key_split": n_split,
+                   **({"tile_override": os.environ["UA_TILE"]} if os.environ.get("UA_TILE") else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},

@@ -57,9 +57,11 @@
 #include "ua_internal.h"
 
 #include <math.h>
+#include <cstdlib>
 
 #include <atomic>
 #include <mutex>
+#include <string>
 #include <type_traits>
 #include <utility>
 
@@ -1255,8 +1257,49 @@ struct LaunchShape {
     int rows() const { return 32 * rb * nw / ks; }
 };
 
+// UA_TILE (environment, read once per process; for tuning): forces the
+// launch shape, as query rows x keys per tile: "256x64" (8 waves), "512x32"
+// (8 waves of two row blocks, d = 64 only), "128x64" (4 waves) or "128x32"
+// (two key groups of 4 waves, an even number of 32-key tiles only).  Any
+// other value, or a shape it does not fit, leaves the choice below.
+enum class TileOverride { none, r256k64, r512k32, r128k64, r128k32 };
+TileOverride tile_override_setting()
+{
+    static const TileOverride v = [] {
+        const char *e = std::getenv("UA_TILE");
+        if (!e) return TileOverride::none;
+        const std::string t(e);
+        if (t == "256x64") return TileOverride::r256k64;
+        if (t == "512x32") return TileOverride::r512k32;
+        if (t == "128x64") return TileOverride::r128k64;
+        if (t == "128x32") return TileOverride::r128k32;
+        return TileOverride::none;
+    }();
+    return v;
+}
+bool tile_override(int64_t S, int d, LaunchShape *ls)
+{
+    switch (tile_override_setting()) {
+    case TileOverride::r256k64: *ls = {8, 1, 64, 1}; return true;
+    case TileOverride::r512k32:
+        if (d != 64) return false;
+        *ls = {8, 2, 32, 1};
+        return true;
+    case TileOverride::r128k64: *ls = {4, 1, 64, 1}; return true;
+    case TileOverride::r128k32: {
+        const int64_t nt = (S + 31) / 32;
+        if (nt < 2 || nt % 2 != 0) return false;
+        *ls = {8, 1, 32, 2};
+        return true;
+    }
+    default: return false;
+    }
+}
+
 LaunchShape launch_shape(int64_t B, int64_t S, int64_t Hl, int d, int64_t cus)
 {
+    LaunchShape forced;
+    if (tile_override(S, d, &forced)) return forced;
     const auto units = [&](int64_t rows) { return B * Hl * ((S + rows - 1) / rows); };
     // rounds of units over the CUs times the rows a unit processes
     const auto cost = [&](int64_t rows) { return (units(rows) + cus - 1) / cus * (S < rows ? S : rows); };
@@ -1328,7 +1371,8 @@ SplitPlan split_plan(int64_t B, int64_t S, int64_t Hl, int d, int64_t cus)
     const int64_t U0 = (S + plain.kb - 1) / plain.kb / plain.ks;
     int64_t best_cost = (units(plain) + cus - 1) / cus * (U0 * plain.kb + kSplitFixedKeys);
     LaunchShape cands[2] = {plain, {8, 1, 64, 1}};
-    const int ncand = plain.rows() == 128 ? 2 : 1;
+    LaunchShape forced;
+    const int ncand = plain.rows() == 128 && !tile_override(S, d, &forced) ? 2 : 1;
     for (int n = 1; n <= kSplitMaxN; ++n)
         for (int c = 0; c < ncand; ++c) {
             const LaunchShape &ls = cands[c];

@@ -46,7 +46,12 @@
  * the launch.  Launch shapes (and so ua_work_units, ua_key_split and the
  * workspace sizes) follow the current device's compute-unit and XCD counts,
  * queried once per device; on a host without a device they are computed for
- * the full MI355X (256 CUs in 8 XCDs).
+ * the full MI355X (256 CUs in 8 XCDs).  For tuning, the environment variable
+ * UA_TILE (read once per process) forces the launch shape, as query rows x
+ * keys per tile: "256x64", "512x32" (d = 64 only), "128x64" or "128x32"
+ * (an even number of 32-key tiles only); other values, or shapes it does
+ * not fit, are ignored.  Results stay within the stated accuracy for any
+ * shape, but their bits may differ between shapes.
  *
  * Errors: every call returns a status code and never prints or aborts.
  * Arguments are validated on the host before any device access, in this

@@ -305,3 +305,31 @@ def test_write_counts_validates_its_counter_buffer():
     assert ua.key_split(1, 16384, 40, 128, 8) > 1
     assert call((1, 16384, 40, 128)) == ua.UA_ERR_NULL
     assert call((1, 16384, 40, 128), ws=A + 8192, ws_bytes=64) == ua.UA_ERR_WORKSPACE
+
+
+def test_tile_override_from_the_environment():
+    """UA_TILE forces the launch shape (read once per process, so each
+    setting runs in a fresh interpreter); unknown values and shapes it does
+    not fit are ignored."""
+    import subprocess
+    import sys
+    code = ("import comm_fusion_amd as ua; print(ua.work_units(2, 32768, 24, 64, 4), "
+            "ua.work_units(1, 65536, 40, 128, 8), ua.work_units(1, 4064, 8, 128, 8), "
+            "ua.key_split(1, 4096, 24, 128, 8))")
+
+    def run(tile):
+        env = dict(os.environ)
+        env.pop("UA_TILE", None)
+        if tile is not None:
+            env["UA_TILE"] = tile
+        out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True,
+                             check=True, timeout=300).stdout
+        return tuple(int(x) for x in out.split())
+
+    default = run(None)
+    assert default == (768, 1280, 32, 2)          # mixed 512-row units, video 256, 4064 keys 128-row
+    assert run("256x64") == (1536, 1280, 16, 4)   # 256-row units everywhere
+    assert run("512x32") == (768, 1280, 32, 2)    # d = 64 only: the d = 128 shapes keep their choice
+    assert run("128x64")[:3] == (3072, 2560, 32)  # 4-wave 128-row units
+    assert run("128x32")[2] == 32                 # 127 key tiles of 32: odd, so ignored there
+    assert run("nonsense") == default
