@@ -581,7 +581,8 @@ def main():
     unsplit = None
     if n_split > 1:
         t_u = med(cmp["unsplit"])
-        unsplit = {"key_split": n_split, "workspace_bytes": ua.workspace_bytes(w.B, w.S, w.H, w.d, w.P),
+        unsplit = {"key_split": n_split, "stream_k_iters": ua.stream_k_iters(w.B, w.S, w.H, w.d, w.P),
+                   "workspace_bytes": ua.workspace_bytes(w.B, w.S, w.H, w.d, w.P),
                    "unsplit_fused_ms_median": round(t_u, 4),
                    "unsplit_TFLOPs": round(w.flops / (t_u * 1e-3) / 1e12, 2),
                    "speedup_split_over_unsplit": round(t_u / t_f, 4),
