@@ -199,7 +199,9 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
 
-    u32x4 fa[2][4], fbr[2][2];
+    // fragment registers: the first k-substep's in two sets (a step's own,
+    // and the next step's, read ahead), the second substep's in one
+    u32x4 fa[3][4], fbr[3][2];
     // the six fragment reads of k-substep KK (0, 1) of the stage ST
     auto reads = [&](auto stc, auto kkc, u32x4 (&da)[4], u32x4 (&db)[2]) {
         constexpr int ST = decltype(stc)::value, KK = decltype(kkc)::value;
@@ -220,50 +222,69 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
                 acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, da[fb]), __builtin_bit_cast(bf16x8, db[tb]), acc[fb][tb], 0, 0, 0);
     };
-    // One k-step on stage ST = s % 4.  Its copies have landed once at most
-    // the later steps' copies already issued (those of s+1 and s+2, 2 NCPW
-    // each) remain in flight; after the barrier every wave is done with step
-    // s-1, whose stage takes the copies of step s+3.
+    // One k-step on stage ST = s % 4.  The copies of steps s and s+1 have
+    // landed once at most those of s+2 (2 NCPW, issued one step earlier)
+    // remain in flight; after the barrier every wave's have, and every wave
+    // is done with step s-1, whose stage takes the copies of step s+3.  The
+    // first k-substep's reads of step s were issued at the end of step s-1
+    // (into set PS = s % 2; those of step 0 by the prologue); the end of
+    // step s issues those of step s+1 into the other set, so the MFMAs of a
+    // step start without waiting for the LDS.  The last step issues them too
+    // (from a stage that is not used any more): no branch, so the compiler
+    // has no reason to move fragment registers while reads are in flight.
     auto step = [&](int s, auto stc) {
-        constexpr int ST = decltype(stc)::value;
-        const int later = nk - 1 - s;   // steps after s
-        if (later >= 2)
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(4 * NCPW) : "memory");
-        else if (later == 1)
+        constexpr int ST = decltype(stc)::value, PS = ST & 1, PN = PS ^ 1;
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using SN = std::integral_constant<int, (ST + 1) & 3>;
+        if (s + 2 < nk)
             asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(2 * NCPW) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (s + 3 < nk) copy(s + 3, (ST + 3) & 3);
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        reads(stc, I0(), fa[0], fbr[0]);
-        reads(stc, I1(), fa[1], fbr[1]);
-        lgkm_wait<6>(fa[0], fbr[0]);
-        mfmas(fa[0], fbr[0]);
+        reads(stc, I1(), fa[2], fbr[2]);
+        lgkm_wait<6>(fa[PS], fbr[PS]);
+        mfmas(fa[PS], fbr[PS]);
         __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait<0>(fa[1], fbr[1]);
-        mfmas(fa[1], fbr[1]);
+        reads(SN(), I0(), fa[PN], fbr[PN]);
+        lgkm_wait<6>(fa[2], fbr[2]);
+        mfmas(fa[2], fbr[2]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: the copies of steps 0, 1, 2
+    // prologue: the copies of steps 0, 1, 2, and once step 0's have landed
+    // everywhere, its first k-substep's reads
     for (int p = 0; p < 3 && p < nk; ++p) copy(p, p);
+    if (nk > 2)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(4 * NCPW) : "memory");
+    else if (nk > 1)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(2 * NCPW) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    reads(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), fa[0], fbr[0]);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using S2 = std::integral_constant<int, 2>;
     using S3 = std::integral_constant<int, 3>;
-    int s = 0;
-    for (; s + 3 < nk; s += 4) {
+    // K is a multiple of 128 (hidden % 256, inter % 128), so nk % 4 == 0
+    for (int s = 0; s < nk; s += 4) {
         step(s, S0());
         step(s + 1, S1());
         step(s + 2, S2());
         step(s + 3, S3());
     }
-    if (s < nk) step(s++, S0());
-    if (s < nk) step(s++, S1());
-    if (s < nk) step(s++, S2());
-    // every wave is done with the operand tiles (the Linear-2 epilogue reuses the LDS)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // every wave is done with the operand tiles (the Linear-2 epilogue reuses
+    // the LDS); the last step's read-ahead lands in one of the two sets, so
+    // both stay reserved until the wait.  The copy offsets stay reserved up
+    // to here too: otherwise their registers, free after the last copies,
+    // may take fragments read ahead in the last steps.
+    static_assert(NCPW == 2, "copy offsets tied below");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier"
+                 : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[0][2]), "+v"(fa[0][3]), "+v"(fbr[0][0]), "+v"(fbr[0][1]),
+                   "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]), "+v"(fbr[1][0]), "+v"(fbr[1][1]),
+                   "+v"(aoff[0]), "+v"(aoff[1]), "+v"(boff[0]), "+v"(boff[1])
+                 :
+                 : "memory");
 
     // Accumulator register r of block (fb, tb) is feature 8(r/4) + 4g + r%4 of
     // the block, token row l32 of the block.
