@@ -15,14 +15,14 @@
 //  * one kernel for both layers: a workgroup of 8 wave64s (two per SIMD)
 //    computes a tile of 256 output features x 256 token rows, each wave
 //    128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (six operand reads
-//    per eight MFMAs), over k-steps of 32;
+//    per eight MFMAs), over k-steps of 64 (four substeps of 16);
 //  * outputs are computed transposed, C^T = W X^T: the weight rows are the A
 //    operand and the token rows the B operand, so every lane holds one token
 //    row and 16 of its features per block (runs of 4 consecutive features);
-//  * operand tiles go global -> LDS directly (no VGPR staging) through a
-//    ring of four stages, each copy issued three k-steps before its use; one
-//    barrier per step; the operand reads are explicit LDS instructions
-//    prefetched a k-substep ahead;
+//  * operand tiles go global -> LDS directly (no VGPR staging) into two
+//    stages, each step's copies issued as the previous step starts; one
+//    barrier per step of 32 MFMAs per wave; the operand reads are explicit
+//    LDS instructions issued a k-substep ahead;
 //  * Linear-1 tiles take 128 gate rows and the 128 matching up rows of W1,
 //    arranged so that each wave's feature blocks hold gate and up of the
 //    same intermediate columns: SiLU(gate) * up is formed in registers;
@@ -52,12 +52,12 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 constexpr int BM = 256;                 // token rows per tile
 constexpr int BF = 256;                 // feature rows per tile (Linear-1: 128 gate + 128 up)
-constexpr int BK = 32;                  // k per step
-constexpr int NSTAGE = 4;               // LDS ring: copies run three steps ahead
+constexpr int BK = 64;                  // k per step
+constexpr int NSTAGE = 2;               // LDS stages: copies run one step ahead
 constexpr int NW = 8;                   // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
-constexpr int TILE = 256 * BK * 2;      // bytes of one operand tile (16 KiB)
-constexpr int STAGE = 2 * TILE;         // W tile + token tile (32 KiB)
+constexpr int TILE = 256 * BK * 2;      // bytes of one operand tile (32 KiB)
+constexpr int STAGE = 2 * TILE;         // W tile + token tile (64 KiB)
 constexpr int NCPW = TILE / 1024 / NW;  // 1 KiB copies per wave per operand tile
 constexpr int L1_COLS = 128;            // intermediate columns per Linear-1 tile
 constexpr int L2_COLS = 256;            // hidden columns per Linear-2 tile
@@ -122,16 +122,18 @@ __device__ __forceinline__ void lgkm_wait(u32x4 (&fa)[4], u32x4 (&fb)[2])
                  : "i"(N));
 }
 
-// One output tile: 256 features x 256 token rows, K in steps of 32.
-// Operand tiles in the LDS: [row][64 B] (the step's 32 k values), the four
-// 16-byte chunks of a row at positions chunk ^ ((row / 4) % 4), so a
-// fragment read (32 rows, one chunk each per half-wave) spreads over all
-// banks.  They are filled by 1 KiB global->LDS copies (lane L of copy c
-// lands at byte 1024 c + 16 L: row 16 c + L / 4, fetching chunk
-// (L % 4) ^ ((L / 16) % 4)) into a ring of four stages: the copies of step
-// s+3 are issued as step s starts, so each has three steps to land.  Wave
-// (wf, wt) computes features 128 wf .. +127 (four 32-row blocks) of token
-// rows 64 wt .. +63 (two).
+// One output tile: 256 features x 256 token rows, K in steps of 64.
+// Operand tiles in the LDS: [row][128 B] (the step's 64 k values), the eight
+// 16-byte chunks of a row at positions chunk ^ ((row / 2) % 8), so that a
+// fragment read (16 rows per quarter-wave, one chunk each) spreads over all
+// banks.  Stage st's weight tile sits at st * TILE and its token tile at
+// (2 + st) * TILE, so every read offset fits the instruction's 16-bit field.
+// The tiles are filled by 1 KiB global->LDS copies (lane L of copy c lands
+// at byte 1024 c + 16 L: row 8 c + L / 8, position L % 8, fetching chunk
+// (L % 8) ^ (4 (c % 2) + L / 16)) into two stages: the copies of step s+1 are
+// issued as step s starts, so each has a step to land.  Wave (wf, wt)
+// computes features 128 wf .. +127 (four 32-row blocks) of token rows
+// 64 wt .. +63 (two).
 template <int KIND>
 __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int n, lds_u8 *lds)
 {
@@ -140,18 +142,19 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     const int wf = wave & 1, wt = wave >> 1;
     const int l32 = lane & 31, g = lane >> 5;
     const int K = KIND == 0 ? a.hidden : a.inter;
-    const int nk = K / BK;
+    const int nk = K / BK;  // K is a multiple of 128: nk is even
     const char *wbase = (const char *)(KIND == 0 ? a.w1 + (int64_t)sg.expert * 2 * a.inter * a.hidden
                                                  : a.w2 + (int64_t)sg.expert * a.hidden * a.inter);
     const char *bbase = (const char *)(KIND == 0 ? a.x : a.act);
 
     // This wave's copies: numbers NCPW wave .. of each operand tile.
-    const unsigned chunk16 = (unsigned)((lane & 3) ^ ((lane >> 4) & 3)) * 16;
+    static_assert(NCPW % 2 == 0, "copy parity is the copy index's parity");
     unsigned aoff[NCPW], boff[NCPW];
 #pragma unroll
     for (int i = 0; i < NCPW; ++i) {
         const int c = NCPW * wave + i;
-        const int r = 16 * c + (lane >> 2);
+        const int r = 8 * c + (lane >> 3);
+        const unsigned chunk16 = (unsigned)((lane & 7) ^ (4 * (i & 1) + (lane >> 4))) * 16;
         // weight row of tile row r: Linear-1 rows 128 h .. 128 h + 63 are gate
         // rows 128 n + 64 h .., rows 128 h + 64 .. the matching up rows, so a
         // wave's feature blocks 0, 1 (gate) and 2, 3 (up) hold the same
@@ -168,28 +171,29 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     }
     auto copy = [&](int s, int st) {
         const unsigned ko = (unsigned)s * BK * 2;
-        lds_u8 *dst = lds + st * STAGE + NCPW * wave * 1024;
+        lds_u8 *dst = lds + st * TILE + NCPW * wave * 1024;
 #pragma unroll
         for (int i = 0; i < NCPW; ++i) {
             __builtin_amdgcn_global_load_lds((gbl_void *)(wbase + aoff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko), (lds_void *)(dst + TILE + i * 1024),
-                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko),
+                                             (lds_void *)(dst + 2 * TILE + i * 1024), 16, 0, 0);
         }
     };
 
-    // Per-lane LDS addresses of the fragment reads; stage and block are
-    // instruction offsets (stages 2 and 3 through their own base registers:
-    // the offset field holds 16 bits).  Fragment element layout: lane l gives
-    // row (block + l % 32), k values 8 (l / 32) .. +7 of the 16-wide
-    // k-substep (substep 0: chunks 0, 1; substep 1: chunks 2, 3).
+    // Per-lane LDS addresses of the fragment reads, one per k-substep KK
+    // (0..3); stage and block are instruction offsets.  Fragment element
+    // layout: lane l gives row (block + l % 32), k values 16 KK + 8 (l / 32)
+    // .. +7, i.e. chunk 2 KK + l / 32, at position chunk ^ ((l % 32 / 2) % 8).
     const unsigned lbase = (unsigned)(uintptr_t)lds;
-    const unsigned sw0 = (unsigned)(((0 + g) ^ ((l32 >> 2) & 3)) * 16);
-    const unsigned sw1 = (unsigned)(((2 + g) ^ ((l32 >> 2) & 3)) * 16);
-    const unsigned ra = lbase + (unsigned)(128 * wf + l32) * 64;
-    const unsigned rb = lbase + TILE + (unsigned)(64 * wt + l32) * 64;
-    // [stage / 2][substep]
-    const unsigned abase[2][2] = {{ra + sw0, ra + sw1}, {ra + 2 * STAGE + sw0, ra + 2 * STAGE + sw1}};
-    const unsigned bbase2[2][2] = {{rb + sw0, rb + sw1}, {rb + 2 * STAGE + sw0, rb + 2 * STAGE + sw1}};
+    const unsigned sw = (unsigned)((l32 >> 1) & 7);
+    const unsigned ra = lbase + (unsigned)(128 * wf + l32) * 128;
+    const unsigned rb = lbase + 2 * TILE + (unsigned)(64 * wt + l32) * 128;
+    unsigned pa[4], pb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        pa[kk] = ra + (((unsigned)(2 * kk + g) ^ sw) * 16);
+        pb[kk] = rb + (((unsigned)(2 * kk + g) ^ sw) * 16);
+    }
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -199,20 +203,22 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[fb][tb][r] = 0.f;
 
-    // fragment registers: the first k-substep's in two sets (a step's own,
-    // and the next step's, read ahead), the second substep's in one
+    // Fragment registers: three sets.  A set is read into again only once
+    // the MFMAs of another set were issued after its own, which have
+    // therefore started and taken their operands.
     u32x4 fa[3][4], fbr[3][2];
-    // the six fragment reads of k-substep KK (0, 1) of the stage ST
-    auto reads = [&](auto stc, auto kkc, u32x4 (&da)[4], u32x4 (&db)[2]) {
-        constexpr int ST = decltype(stc)::value, KK = decltype(kkc)::value;
-        constexpr int OFF = (ST & 1) * STAGE;
-        const unsigned pa = abase[ST >> 1][KK], pb = bbase2[ST >> 1][KK];
-        da[0] = lds_read<OFF + 0 * 2048>(pa);
-        da[1] = lds_read<OFF + 1 * 2048>(pa);
-        da[2] = lds_read<OFF + 2 * 2048>(pa);
-        da[3] = lds_read<OFF + 3 * 2048>(pa);
-        db[0] = lds_read<OFF + 0 * 2048>(pb);
-        db[1] = lds_read<OFF + 1 * 2048>(pb);
+    // the six fragment reads of k-substep KK of stage ST into set SET
+    auto reads = [&](auto stc, auto kkc, auto setc) {
+        constexpr int ST = decltype(stc)::value, KK = decltype(kkc)::value, SET = decltype(setc)::value;
+        constexpr int OFF = ST * TILE;
+        u32x4 (&da)[4] = fa[SET];
+        u32x4 (&db)[2] = fbr[SET];
+        da[0] = lds_read<OFF + 0 * 4096>(pa[KK]);
+        da[1] = lds_read<OFF + 1 * 4096>(pa[KK]);
+        da[2] = lds_read<OFF + 2 * 4096>(pa[KK]);
+        da[3] = lds_read<OFF + 3 * 4096>(pa[KK]);
+        db[0] = lds_read<OFF + 0 * 4096>(pb[KK]);
+        db[1] = lds_read<OFF + 1 * 4096>(pb[KK]);
     };
     auto mfmas = [&](u32x4 (&da)[4], u32x4 (&db)[2]) {
 #pragma unroll
@@ -222,69 +228,70 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
                 acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, da[fb]), __builtin_bit_cast(bf16x8, db[tb]), acc[fb][tb], 0, 0, 0);
     };
-    // One k-step on stage ST = s % 4.  The copies of steps s and s+1 have
-    // landed once at most those of s+2 (2 NCPW, issued one step earlier)
-    // remain in flight; after the barrier every wave's have, and every wave
-    // is done with step s-1, whose stage takes the copies of step s+3.  The
-    // first k-substep's reads of step s were issued at the end of step s-1
-    // (into set PS = s % 2; those of step 0 by the prologue); the end of
-    // step s issues those of step s+1 into the other set, so the MFMAs of a
-    // step start without waiting for the LDS.  The last step issues them too
-    // (from a stage that is not used any more): no branch, so the compiler
-    // has no reason to move fragment registers while reads are in flight.
-    auto step = [&](int s, auto stc) {
-        constexpr int ST = decltype(stc)::value, PS = ST & 1, PN = PS ^ 1;
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using SN = std::integral_constant<int, (ST + 1) & 3>;
-        if (s + 2 < nk)
-            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(2 * NCPW) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + 3 < nk) copy(s + 3, (ST + 3) & 3);
-        reads(stc, I1(), fa[2], fbr[2]);
-        lgkm_wait<6>(fa[PS], fbr[PS]);
-        mfmas(fa[PS], fbr[PS]);
+    // One k-step on stage ST = s % 2.  Its copies (issued as step s-1
+    // started) have landed once none of this wave's remain in flight; after
+    // the barrier every wave's have, and every wave is done with step s-1,
+    // whose stage takes the copies of step s+1.  Each substep's reads are
+    // issued before the previous substep's MFMAs; all are waited for within
+    // the step.  PH = s % 3 (substep 4 s + j uses set (PH + j) % 3).
+    auto step = [&](int s, auto stc, auto phc) {
+        constexpr int ST = decltype(stc)::value, PH = decltype(phc)::value;
+        constexpr int A = PH % 3, B = (PH + 1) % 3, C = (PH + 2) % 3;  // sets of substeps 0 (and 3), 1, 2
+        using K0 = std::integral_constant<int, 0>;
+        using K1 = std::integral_constant<int, 1>;
+        using K2 = std::integral_constant<int, 2>;
+        using K3 = std::integral_constant<int, 3>;
+        using SA = std::integral_constant<int, A>;
+        using SB = std::integral_constant<int, B>;
+        using SC = std::integral_constant<int, C>;
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + 1 < nk) copy(s + 1, ST ^ 1);
+        reads(stc, K0(), SA());
+        reads(stc, K1(), SB());
+        lgkm_wait<6>(fa[A], fbr[A]);
+        mfmas(fa[A], fbr[A]);
         __builtin_amdgcn_sched_barrier(0);
-        reads(SN(), I0(), fa[PN], fbr[PN]);
-        lgkm_wait<6>(fa[2], fbr[2]);
-        mfmas(fa[2], fbr[2]);
+        reads(stc, K2(), SC());
+        lgkm_wait<6>(fa[B], fbr[B]);
+        mfmas(fa[B], fbr[B]);
+        __builtin_amdgcn_sched_barrier(0);
+        reads(stc, K3(), SA());
+        lgkm_wait<6>(fa[C], fbr[C]);
+        mfmas(fa[C], fbr[C]);
+        __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait<0>(fa[A], fbr[A]);
+        mfmas(fa[A], fbr[A]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: the copies of steps 0, 1, 2, and once step 0's have landed
-    // everywhere, its first k-substep's reads
-    for (int p = 0; p < 3 && p < nk; ++p) copy(p, p);
-    if (nk > 2)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(4 * NCPW) : "memory");
-    else if (nk > 1)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(2 * NCPW) : "memory");
-    else
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    reads(std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), fa[0], fbr[0]);
+    // prologue: the copies of step 0; then the steps, six at a time (stage
+    // s % 2, register phase s % 3 fixed at compile time), and the last 0, 2
+    // or 4 (nk is even)
+    copy(0, 0);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
-    // K is a multiple of 128 (hidden % 256, inter % 128), so nk % 4 == 0
-    for (int s = 0; s < nk; s += 4) {
-        step(s, S0());
-        step(s + 1, S1());
-        step(s + 2, S2());
-        step(s + 3, S3());
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    int s = 0;
+    for (; s + 6 <= nk; s += 6) {
+        step(s, S0(), P0());
+        step(s + 1, S1(), P1());
+        step(s + 2, S0(), P2());
+        step(s + 3, S1(), P0());
+        step(s + 4, S0(), P1());
+        step(s + 5, S1(), P2());
     }
-    // every wave is done with the operand tiles (the Linear-2 epilogue reuses
-    // the LDS); the last step's read-ahead lands in one of the two sets, so
-    // both stay reserved until the wait.  The copy offsets stay reserved up
-    // to here too: otherwise their registers, free after the last copies,
-    // may take fragments read ahead in the last steps.
-    static_assert(NCPW == 2, "copy offsets tied below");
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier"
-                 : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fa[0][2]), "+v"(fa[0][3]), "+v"(fbr[0][0]), "+v"(fbr[0][1]),
-                   "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fa[1][2]), "+v"(fa[1][3]), "+v"(fbr[1][0]), "+v"(fbr[1][1]),
-                   "+v"(aoff[0]), "+v"(aoff[1]), "+v"(boff[0]), "+v"(boff[1])
-                 :
-                 : "memory");
+    if (s < nk) {
+        step(s, S0(), P0());
+        step(s + 1, S1(), P1());
+    }
+    if (s + 2 < nk) {
+        step(s + 2, S0(), P2());
+        step(s + 3, S1(), P0());
+    }
+    // every wave is done with the operand tiles (the Linear-2 epilogue reuses the LDS)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // Accumulator register r of block (fb, tb) is feature 8(r/4) + 4g + r%4 of
     // the block, token row l32 of the block.
@@ -369,6 +376,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 void moe_tiles(MoeArgs a)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char lds_all[NSTAGE * STAGE];  // 128 KiB: one workgroup per CU
+    static_assert(NSTAGE * STAGE >= BM * 512, "the Linear-2 epilogue stages 256 rows of 512 bytes");
     lds_u8 *const lds = (lds_u8 *)lds_all;
     const int64_t N = (int64_t)a.n_l1 + a.n_l2;
     const int64_t b = xcd_block(blockIdx.x, N, a.n_xcd);
