@@ -19,10 +19,11 @@
 //  * outputs are computed transposed, C^T = W X^T: the weight rows are the A
 //    operand and the token rows the B operand, so every lane holds one token
 //    row and 16 of its features per block (runs of 4 consecutive features);
-//  * operand tiles go global -> LDS directly (no VGPR staging) into two
-//    stages, each step's copies issued as the previous step starts; one
-//    barrier per step of 32 MFMAs per wave; the operand reads are explicit
-//    LDS instructions issued a k-substep ahead;
+//  * operand tiles go global -> LDS directly (no VGPR staging): weight tiles
+//    (mostly from HBM) through three stages, copied two k-steps ahead, token
+//    tiles (mostly L2 hits) through two, one step ahead; one barrier per
+//    step of 32 MFMAs per wave; the operand reads are explicit LDS
+//    instructions issued a k-substep ahead;
 //  * Linear-1 tiles take 128 gate rows and the 128 matching up rows of W1,
 //    arranged so that each wave's feature blocks hold gate and up of the
 //    same intermediate columns: SiLU(gate) * up is formed in registers;
@@ -53,11 +54,12 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 constexpr int BM = 256;                 // token rows per tile
 constexpr int BF = 256;                 // feature rows per tile (Linear-1: 128 gate + 128 up)
 constexpr int BK = 64;                  // k per step
-constexpr int NSTAGE = 2;               // LDS stages: copies run one step ahead
+constexpr int NSTAGE_W = 3;             // weight tile stages: copies run two steps ahead
+constexpr int NSTAGE_X = 2;             // token tile stages: copies run one step ahead
 constexpr int NW = 8;                   // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
 constexpr int TILE = 256 * BK * 2;      // bytes of one operand tile (32 KiB)
-constexpr int STAGE = 2 * TILE;         // W tile + token tile (64 KiB)
+constexpr int LDS_BYTES = (NSTAGE_W + NSTAGE_X) * TILE;  // 160 KiB
 constexpr int NCPW = TILE / 1024 / NW;  // 1 KiB copies per wave per operand tile
 constexpr int L1_COLS = 128;            // intermediate columns per Linear-1 tile
 constexpr int L2_COLS = 256;            // hidden columns per Linear-2 tile
@@ -126,12 +128,11 @@ __device__ __forceinline__ void lgkm_wait(u32x4 (&fa)[4], u32x4 (&fb)[2])
 // Operand tiles in the LDS: [row][128 B] (the step's 64 k values), the eight
 // 16-byte chunks of a row at positions chunk ^ ((row / 2) % 8), so that a
 // fragment read (16 rows per quarter-wave, one chunk each) spreads over all
-// banks.  Stage st's weight tile sits at st * TILE and its token tile at
-// (2 + st) * TILE, so every read offset fits the instruction's 16-bit field.
-// The tiles are filled by 1 KiB global->LDS copies (lane L of copy c lands
-// at byte 1024 c + 16 L: row 8 c + L / 8, position L % 8, fetching chunk
-// (L % 8) ^ (4 (c % 2) + L / 16)) into two stages: the copies of step s+1 are
-// issued as step s starts, so each has a step to land.  Wave (wf, wt)
+// banks.  Weight stage w sits at w * TILE (w = 0, 1, 2), token stage x at
+// (3 + x) * TILE.  The tiles are filled by 1 KiB global->LDS copies (lane L
+// of copy c lands at byte 1024 c + 16 L: row 8 c + L / 8, position L % 8,
+// fetching chunk (L % 8) ^ (4 (c % 2) + L / 16)): as step s starts, the
+// token tile of step s+1 and then the weight tile of step s+2.  Wave (wf, wt)
 // computes features 128 wf .. +127 (four 32-row blocks) of token rows
 // 64 wt .. +63 (two).
 template <int KIND>
@@ -169,15 +170,20 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         const unsigned brow = KIND == 0 ? (unsigned)(a.row_slot[ri] / a.k) : (unsigned)ri;
         boff[i] = brow * (unsigned)K * 2 + chunk16;
     }
-    auto copy = [&](int s, int st) {
+    // weight tile of step s into weight stage w; token tile into token stage x
+    auto copy_w = [&](int s, int w) {
         const unsigned ko = (unsigned)s * BK * 2;
-        lds_u8 *dst = lds + st * TILE + NCPW * wave * 1024;
+        lds_u8 *dst = lds + w * TILE + NCPW * wave * 1024;
 #pragma unroll
-        for (int i = 0; i < NCPW; ++i) {
+        for (int i = 0; i < NCPW; ++i)
             __builtin_amdgcn_global_load_lds((gbl_void *)(wbase + aoff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko),
-                                             (lds_void *)(dst + 2 * TILE + i * 1024), 16, 0, 0);
-        }
+    };
+    auto copy_x = [&](int s, int x) {
+        const unsigned ko = (unsigned)s * BK * 2;
+        lds_u8 *dst = lds + (NSTAGE_W + x) * TILE + NCPW * wave * 1024;
+#pragma unroll
+        for (int i = 0; i < NCPW; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
     };
 
     // Per-lane LDS addresses of the fragment reads, one per k-substep KK
@@ -187,11 +193,13 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     const unsigned lbase = (unsigned)(uintptr_t)lds;
     const unsigned sw = (unsigned)((l32 >> 1) & 7);
     const unsigned ra = lbase + (unsigned)(128 * wf + l32) * 128;
-    const unsigned rb = lbase + 2 * TILE + (unsigned)(64 * wt + l32) * 128;
-    unsigned pa[4], pb[4];
+    const unsigned rb = lbase + NSTAGE_W * TILE + (unsigned)(64 * wt + l32) * 128;
+    // weight stage 2 through its own bases (offset past the 16-bit field)
+    unsigned pa[4], pa2[4], pb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         pa[kk] = ra + (((unsigned)(2 * kk + g) ^ sw) * 16);
+        pa2[kk] = pa[kk] + 2 * TILE;
         pb[kk] = rb + (((unsigned)(2 * kk + g) ^ sw) * 16);
     }
 
@@ -207,18 +215,21 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     // the MFMAs of another set were issued after its own, which have
     // therefore started and taken their operands.
     u32x4 fa[3][4], fbr[3][2];
-    // the six fragment reads of k-substep KK of stage ST into set SET
-    auto reads = [&](auto stc, auto kkc, auto setc) {
-        constexpr int ST = decltype(stc)::value, KK = decltype(kkc)::value, SET = decltype(setc)::value;
-        constexpr int OFF = ST * TILE;
+    // the six fragment reads of k-substep KK of weight stage WS and token
+    // stage XS into set SET
+    auto reads = [&](auto wsc, auto xsc, auto kkc, auto setc) {
+        constexpr int WS = decltype(wsc)::value, XS = decltype(xsc)::value;
+        constexpr int KK = decltype(kkc)::value, SET = decltype(setc)::value;
+        constexpr int OA = (WS & 1) * TILE, OB = XS * TILE;
+        const unsigned p = WS == 2 ? pa2[KK] : pa[KK];
         u32x4 (&da)[4] = fa[SET];
         u32x4 (&db)[2] = fbr[SET];
-        da[0] = lds_read<OFF + 0 * 4096>(pa[KK]);
-        da[1] = lds_read<OFF + 1 * 4096>(pa[KK]);
-        da[2] = lds_read<OFF + 2 * 4096>(pa[KK]);
-        da[3] = lds_read<OFF + 3 * 4096>(pa[KK]);
-        db[0] = lds_read<OFF + 0 * 4096>(pb[KK]);
-        db[1] = lds_read<OFF + 1 * 4096>(pb[KK]);
+        da[0] = lds_read<OA + 0 * 4096>(p);
+        da[1] = lds_read<OA + 1 * 4096>(p);
+        da[2] = lds_read<OA + 2 * 4096>(p);
+        da[3] = lds_read<OA + 3 * 4096>(p);
+        db[0] = lds_read<OB + 0 * 4096>(pb[KK]);
+        db[1] = lds_read<OB + 1 * 4096>(pb[KK]);
     };
     auto mfmas = [&](u32x4 (&da)[4], u32x4 (&db)[2]) {
 #pragma unroll
@@ -228,14 +239,18 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
                 acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, da[fb]), __builtin_bit_cast(bf16x8, db[tb]), acc[fb][tb], 0, 0, 0);
     };
-    // One k-step on stage ST = s % 2.  Its copies (issued as step s-1
-    // started) have landed once none of this wave's remain in flight; after
-    // the barrier every wave's have, and every wave is done with step s-1,
-    // whose stage takes the copies of step s+1.  Each substep's reads are
-    // issued before the previous substep's MFMAs; all are waited for within
-    // the step.  PH = s % 3 (substep 4 s + j uses set (PH + j) % 3).
-    auto step = [&](int s, auto stc, auto phc) {
-        constexpr int ST = decltype(stc)::value, PH = decltype(phc)::value;
+    // One k-step on weight stage s % 3 and token stage s % 2.  Its copies
+    // (weights issued as step s-2 started, tokens as step s-1 started,
+    // before the weights of step s+1) have landed once at most the weight
+    // copies of step s+1 remain in flight; after the barrier every wave's
+    // have, and every wave is done with step s-1, whose stages take the
+    // token tile of step s+1 and the weight tile of step s+2.  Each
+    // substep's reads are issued before the previous substep's MFMAs; all
+    // are waited for within the step.  PH = s % 3 also picks the fragment
+    // register sets (substep 4 s + j uses set (PH + j) % 3).
+    auto step = [&](int s, auto xsc, auto phc) {
+        constexpr int XS = decltype(xsc)::value, PH = decltype(phc)::value;
+        using WS = std::integral_constant<int, PH>;
         constexpr int A = PH % 3, B = (PH + 1) % 3, C = (PH + 2) % 3;  // sets of substeps 0 (and 3), 1, 2
         using K0 = std::integral_constant<int, 0>;
         using K1 = std::integral_constant<int, 1>;
@@ -244,18 +259,22 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         using SA = std::integral_constant<int, A>;
         using SB = std::integral_constant<int, B>;
         using SC = std::integral_constant<int, C>;
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        if (s + 1 < nk) copy(s + 1, ST ^ 1);
-        reads(stc, K0(), SA());
-        reads(stc, K1(), SB());
+        if (s + 1 < nk)
+            asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(NCPW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        if (s + 1 < nk) copy_x(s + 1, XS ^ 1);
+        if (s + 2 < nk) copy_w(s + 2, (PH + 2) % 3);
+        reads(WS(), xsc, K0(), SA());
+        reads(WS(), xsc, K1(), SB());
         lgkm_wait<6>(fa[A], fbr[A]);
         mfmas(fa[A], fbr[A]);
         __builtin_amdgcn_sched_barrier(0);
-        reads(stc, K2(), SC());
+        reads(WS(), xsc, K2(), SC());
         lgkm_wait<6>(fa[B], fbr[B]);
         mfmas(fa[B], fbr[B]);
         __builtin_amdgcn_sched_barrier(0);
-        reads(stc, K3(), SA());
+        reads(WS(), xsc, K3(), SA());
         lgkm_wait<6>(fa[C], fbr[C]);
         mfmas(fa[C], fbr[C]);
         __builtin_amdgcn_sched_barrier(0);
@@ -264,10 +283,12 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: the copies of step 0; then the steps, six at a time (stage
-    // s % 2, register phase s % 3 fixed at compile time), and the last 0, 2
-    // or 4 (nk is even)
-    copy(0, 0);
+    // prologue: the weight and token tiles of step 0, the weight tile of
+    // step 1; then the steps, six at a time (stages and register sets fixed
+    // at compile time), and the last 0, 2 or 4 (nk is even)
+    copy_w(0, 0);
+    copy_x(0, 0);
+    copy_w(1, 1);
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using P0 = std::integral_constant<int, 0>;
@@ -375,8 +396,8 @@ __device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t n, int64_t nx)
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void moe_tiles(MoeArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[NSTAGE * STAGE];  // 128 KiB: one workgroup per CU
-    static_assert(NSTAGE * STAGE >= BM * 512, "the Linear-2 epilogue stages 256 rows of 512 bytes");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[LDS_BYTES];  // 160 KiB: one workgroup per CU
+    static_assert(LDS_BYTES >= BM * 512, "the Linear-2 epilogue stages 256 rows of 512 bytes");
     lds_u8 *const lds = (lds_u8 *)lds_all;
     const int64_t N = (int64_t)a.n_l1 + a.n_l2;
     const int64_t b = xcd_block(blockIdx.x, N, a.n_xcd);
