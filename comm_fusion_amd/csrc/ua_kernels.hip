@@ -22,8 +22,8 @@
 //    v_mfma_f32_32x32x16_bf16: K streams from LDS as the A operand and the
 //    wave's Q rows stay in VGPRs as the B operand.  The accumulator layout
 //    then gives every lane ONE query row (lane % 32) and 16 keys per block,
-//    so the row max needs one v_permlane32_swap per KV tile and the row sum
-//    none until the end;
+//    so a row max needs one v_permlane32_swap and the row sum none until the
+//    end;
 //  * P^T is fed from those registers (rounded to bf16) as the B operand of
 //    O^T += V^T P^T; V^T comes from the key-major V tile through the gfx950
 //    transposing LDS read ds_read_b64_tr_b16;
@@ -36,7 +36,10 @@
 //    softmax of S_t with the MFMAs of O += V_{t-1} P_{t-1} and of S_{t+1},
 //    one MFMA plus a slice of softmax VALU work per issue slot, so every
 //    wave keeps its matrix pipe fed while it does its exponentials;
-//  * online softmax in fp32, log2 domain, with a lazily raised running max;
+//  * online softmax in fp32, log2 domain, with a lazily raised running max:
+//    the tiles between a work item's first and last take P against the max
+//    as it stands (no tile max in the loop) and go to an exact path only
+//    when a lane's sum of the tile's P passes 2^15;
 //  * epilogue: each lane normalises its row and stores it straight to the
 //    destination slot computed from (rank, P) -- the fused All-to-All.  The
 //    local (serial) output is the same epilogue with one region;
