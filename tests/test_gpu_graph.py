@@ -107,3 +107,64 @@ def test_key_split_call_replays_from_a_graph():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_moe_experts_combine_replays_from_a_graph():
+    """The MoE path (several launches per call, both schedules) inside a
+    graph: every replay bit-equal to the eager call; routing weights doubled
+    in place (exact in fp32, and the weighted output is rounded once) show up
+    in the next replay."""
+    import torch
+    from moe_inputs import MOE_SENTINEL_BITS, MOE_WORKLOADS, moe_tensors
+    w = MOE_WORKLOADS["moe_small_skewed"]
+    x, idx, tw, W1, W2 = moe_tensors(w)
+    off, slots = ua.moe_recv_layout(idx, w.rank, w.P, w.hidden, w.inter, w.E)
+    N = int(off[-1])
+    dx, dW1, dW2 = (to_dev(a) for a in (x, W1, W2))
+    dtw = torch.from_numpy(np.ascontiguousarray(tw)).cuda()
+    drs = torch.from_numpy(slots.astype(np.int32)).cuda()
+    act = torch.empty(N * w.inter, dtype=torch.bfloat16, device="cuda")
+    sentinel = MOE_SENTINEL_BITS - 0x10000 if MOE_SENTINEL_BITS >= 0x8000 else MOE_SENTINEL_BITS
+    n_out = w.P * w.T * w.k * w.hidden
+    outs = [torch.full((n_out,), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16) for _ in range(2)]
+
+    def calls():
+        ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, outs[0], act,
+                               schedule=ua.MOE_INTERLEAVED, experts_per_wave=3)
+        ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, outs[1], act,
+                               schedule=ua.MOE_EXPERT_WAVE, experts_per_wave=3)
+
+    calls()
+    torch.cuda.synchronize()
+    refs = [o.clone() for o in outs]
+    assert torch.equal(refs[0].view(torch.int16), refs[1].view(torch.int16))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for _ in range(3):
+        for o in outs:
+            o.view(torch.int16).fill_(sentinel)
+        act.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, refs):
+            assert torch.equal(o.view(torch.int16), r.view(torch.int16))
+
+    dtw.mul_(2)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    served = torch.zeros(w.P * w.T * w.k, dtype=torch.bool, device="cuda")
+    served[drs.long()] = True
+    got = outs[0].view(-1, w.hidden)[served].float()
+    ref = refs[0].view(-1, w.hidden)[served].float()
+    assert torch.equal(got, ref * 2)
+    assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16))
