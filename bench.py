@@ -33,9 +33,11 @@ Prints ONE JSON line:
             fraction of the bf16 peak, traced clock and DVFS flag) for each
             long-sequence workload: video_dit, dit_long and mixed;
   detail.moe  the MoE expert path of one expert-parallel rank (DeepSeek-style
-            layer shape, balanced and skewed routing): the fused call under
-            the Expert-Wave and the interleaved schedule, the serial form
-            (experts, then a separate Combine scatter) and its halves;
+            layer shape, balanced and skewed routing): the fused call in its
+            persistent form (one launch, a device tile queue) under the
+            Expert-Wave and the interleaved schedule, the same calls as one
+            launch per wave, and the serial form (experts, then a separate
+            Combine scatter) and its halves;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -464,8 +466,8 @@ MOE_CONFIGS = ("moe_ds", "moe_ds_skewed")
 class MoeCase:
     """The MoE expert path of one rank at full size: tokens, routing and this
     rank's expert weights resident in HBM, the Combine buffer, and the timed
-    callables (both schedules of the fused call, the serial form and its
-    halves)."""
+    callables (both schedules of the fused call in the persistent form and
+    as one launch per wave, the serial form and its halves)."""
 
     def __init__(self, ua, torch, w, dev, G, weights=None):
         from moe_inputs import moe_rank_weights, moe_tokens
@@ -487,12 +489,18 @@ class MoeCase:
         act = torch.empty(self.N * w.inter, dtype=torch.bfloat16, device=dev)
         comb = torch.empty(w.P * w.T * w.k * w.hidden, dtype=torch.bfloat16, device=dev)
         y = torch.empty(self.N * w.hidden, dtype=torch.bfloat16, device=dev)
+        ws = ua.new_moe_workspace(dx, dW1, dtw, w.P, w.E)
+        self.ws = ws
 
         def fused(schedule):
+            return lambda: ua.moe_experts_combine_ws(dx, drs, dtw, off, dW1, dW2, w.P, w.E, comb, act, ws,
+                                                     schedule=schedule, experts_per_wave=G)
+
+        def per_wave(schedule):
             return lambda: ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, comb, act,
                                                   schedule=schedule, experts_per_wave=G)
-        alone = lambda: ua.moe_experts_local(dx, drs, dtw, off, dW1, dW2, w.P, w.E, y, act,  # noqa: E731
-                                             experts_per_wave=G)
+        alone = lambda: ua.moe_experts_local_ws(dx, drs, dtw, off, dW1, dW2, w.P, w.E, y, act, ws,  # noqa: E731
+                                                experts_per_wave=G)
         scatter = lambda: ua.moe_combine_scatter(y, drs, self.N, w.P, w.T, w.hidden, w.inter, w.E, w.k,  # noqa: E731
                                                  comb)
 
@@ -501,10 +509,13 @@ class MoeCase:
             scatter()
 
         self.fns = {"interleaved": fused(ua.MOE_INTERLEAVED), "expert_wave": fused(ua.MOE_EXPERT_WAVE),
+                    "per_wave_interleaved": per_wave(ua.MOE_INTERLEAVED),
+                    "per_wave_expert_wave": per_wave(ua.MOE_EXPERT_WAVE),
                     "serial": serial, "experts_alone": alone, "scatter": scatter}
         torch.cuda.synchronize()
 
     def measure(self, warmup, rounds):
+        import torch
         w = self.w
         warm_up(self.fns["interleaved"], warmup, WARM_MS)
         warm_up(self.fns["expert_wave"], 1, 50.0)
@@ -518,9 +529,13 @@ class MoeCase:
             "workload": w.name, "routing": w.routing, "P": w.P, "rank": w.rank, "T": w.T, "hidden": w.hidden,
             "inter": w.inter, "E": w.E, "k": w.k, "rows_N": self.N,
             "rows_per_expert_min_max": [int(self.rows_per_expert.min()), int(self.rows_per_expert.max())],
-            "experts_per_wave": self.G, "flops": flops,
+            "experts_per_wave": self.G, "flops": flops, "form": "persistent",
             "interleaved_ms_median": round(med["interleaved"], 4),
             "expert_wave_ms_median": round(med["expert_wave"], 4),
+            "per_wave_launches_interleaved_ms_median": round(med["per_wave_interleaved"], 4),
+            "per_wave_launches_expert_wave_ms_median": round(med["per_wave_expert_wave"], 4),
+            "speedup_persistent_over_per_wave_launches": round(med["per_wave_interleaved"] / med["interleaved"], 4),
+            "bounded_waits_given_up": int(self.ws.view(torch.int32)[32]),
             "speedup_interleaved_over_expert_wave": round(med["expert_wave"] / med["interleaved"], 4),
             "serial_ms_median": round(med["serial"], 4),
             "experts_alone_ms_median": round(med["experts_alone"], 4),

@@ -26,6 +26,9 @@ the MoE expert path with the Combine fused into Linear-2 (include/moe_combine.h)
   moe_experts_combine(x, row_slot, topk_w, expert_offsets, W1, W2, P, E, combine, act,
                       schedule=MOE_INTERLEAVED, experts_per_wave=4, stream=None)
   moe_experts_local(...), moe_combine_scatter(...)   (the serial form)
+  moe_experts_combine_ws(..., act, workspace, schedule=..., experts_per_wave=..., stream=None),
+  moe_experts_local_ws(...)   (the persistent form: one launch, a device tile queue)
+  moe_workspace_bytes(P, T, hidden, inter, E, k), new_moe_workspace(x, W1, topk_w, P, E)
 and, for measurement only,
   attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None)
   epilogue_store_only(B, S, H, d, rank, P, out, stream=None)
@@ -46,4 +49,5 @@ from ._binding import (UA_ERR_ALIGN, UA_ERR_HIP, UA_ERR_NULL, UA_ERR_RANK,  # no
                        new_workspace, status_string, stream_k_iters, version, work_units, workspace_bytes,
                        workspace_count_bytes)
 from ._moe_binding import (MOE_EXPERT_WAVE, MOE_INTERLEAVED, MOE_MAX_WAVE, MoeShape,  # noqa: F401,E402
-                           moe_combine_scatter, moe_experts_combine, moe_experts_local, moe_recv_layout)
+                           moe_combine_scatter, moe_experts_combine, moe_experts_combine_ws, moe_experts_local,
+                           moe_experts_local_ws, moe_recv_layout, moe_workspace_bytes, new_moe_workspace)

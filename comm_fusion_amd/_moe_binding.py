@@ -37,6 +37,12 @@ def _lib():
         L.moe_experts_local.restype = i
         L.moe_combine_scatter.argtypes = [vp, vp, i64, i, sp, vp, vp]
         L.moe_combine_scatter.restype = i
+        L.moe_workspace_bytes.argtypes = [i, sp]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_experts_combine_ws.argtypes = [vp, vp, vp, vp, vp, vp, i, sp, vp, vp, i, i, vp, ctypes.c_size_t, vp]
+        L.moe_experts_combine_ws.restype = i
+        L.moe_experts_local_ws.argtypes = [vp, vp, vp, vp, vp, vp, i, sp, vp, vp, i, vp, ctypes.c_size_t, vp]
+        L.moe_experts_local_ws.restype = i
         _set = True
     return L
 
@@ -102,6 +108,57 @@ def moe_experts_combine(x, row_slot, topk_w, expert_offsets, W1, W2, P, E, combi
                                     int(experts_per_wave), _stream(stream, x, W1, W2, combine, act))
     if st != UA_OK:
         raise UAError("moe_experts_combine", st)
+
+
+def moe_workspace_bytes(P, T, hidden, inter, E, k) -> int:
+    """Bytes of the persistent form's workspace for this shape (0 if invalid)."""
+    return int(_lib().moe_workspace_bytes(int(P), ctypes.byref(MoeShape(T, hidden, inter, E, k))))
+
+
+def new_moe_workspace(x, W1, topk_w, P, E):
+    """A uint8 device tensor of moe_workspace_bytes for the call's shape."""
+    import torch
+    T, hidden = int(x.shape[1]), int(x.shape[2])
+    n = moe_workspace_bytes(P, T, hidden, int(W1.shape[1]) // 2, E, int(topk_w.shape[-1]))
+    return torch.empty(n, dtype=torch.uint8, device=x.device)
+
+
+def _ws(workspace):
+    import torch
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous GPU tensor")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def moe_experts_combine_ws(x, row_slot, topk_w, expert_offsets, W1, W2, P, E, combine, act, workspace,
+                           schedule=MOE_INTERLEAVED, experts_per_wave=4, stream=None):
+    """moe_experts_combine in the persistent form; workspace from new_moe_workspace."""
+    shp = _shape(x, W1, W2, row_slot, topk_w, P, E, combine,
+                 P * int(x.shape[1]) * int(topk_w.shape[-1]), act)
+    off = np.ascontiguousarray(expert_offsets, dtype=np.int64)
+    if off.shape != (E // P + 1,) or int(off[-1]) != row_slot.numel():
+        raise ValueError("expert_offsets must hold E/P + 1 offsets ending at len(row_slot)")
+    wp, wb = _ws(workspace)
+    st = _lib().moe_experts_combine_ws(_ptr(x), _ptr(row_slot), _ptr(topk_w), off.ctypes.data, _ptr(W1), _ptr(W2),
+                                       int(P), ctypes.byref(shp), _ptr(combine), _ptr(act), int(schedule),
+                                       int(experts_per_wave), wp, wb, _stream(stream, x, W1, W2, combine, act))
+    if st != UA_OK:
+        raise UAError("moe_experts_combine_ws", st)
+
+
+def moe_experts_local_ws(x, row_slot, topk_w, expert_offsets, W1, W2, P, E, y_local, act, workspace,
+                         experts_per_wave=4, stream=None):
+    """moe_experts_local in the persistent form."""
+    shp = _shape(x, W1, W2, row_slot, topk_w, P, E, y_local, row_slot.numel(), act)
+    off = np.ascontiguousarray(expert_offsets, dtype=np.int64)
+    if off.shape != (E // P + 1,) or int(off[-1]) != row_slot.numel():
+        raise ValueError("expert_offsets must hold E/P + 1 offsets ending at len(row_slot)")
+    wp, wb = _ws(workspace)
+    st = _lib().moe_experts_local_ws(_ptr(x), _ptr(row_slot), _ptr(topk_w), off.ctypes.data, _ptr(W1), _ptr(W2),
+                                     int(P), ctypes.byref(shp), _ptr(y_local), _ptr(act), int(experts_per_wave),
+                                     wp, wb, _stream(stream, x, W1, W2, y_local, act))
+    if st != UA_OK:
+        raise UAError("moe_experts_local_ws", st)
 
 
 def moe_experts_local(x, row_slot, topk_w, expert_offsets, W1, W2, P, E, y_local, act,

@@ -2,7 +2,8 @@
 // (declared in include/moe_combine.h; part of libulysses_attn.so).
 //
 // Host-side only: argument validation (no device access), the receive layout
-// of a rank, and launches.  The library allocates nothing.
+// of a rank, and launches.  The library allocates nothing: the persistent
+// form's counters live in the caller's workspace.
 
 #include "moe_combine.h"
 
@@ -48,9 +49,20 @@ int check_offsets(const int64_t *off, int64_t E_l, const moe_shape *shp, int P, 
     return UA_OK;
 }
 
+// Words of the persistent form's workspace for these offsets, or -1 when
+// the call needs more launches than the header holds queue counters for.
+int64_t ws_words(const int64_t *offsets, int64_t E_l, int per_wave)
+{
+    const int64_t waves = (E_l + per_wave - 1) / per_wave, per_launch = moe::kMaxWave / per_wave;
+    if ((waves + per_launch - 1) / per_launch > moe::kMaxLaunches) return -1;
+    return moe::kWsHeader + moe::token_tiles(offsets, E_l);
+}
+
+// persistent: run the persistent form with `ws` (ws_bytes) as its counters
 int experts_call(const void *x, const int32_t *row_slot, const float *topk_w, const int64_t *offsets,
                  const void *W1, const void *W2, int P, const moe_shape *shp, void *out, void *act,
-                 int schedule, int per_wave, bool local, hipStream_t stream)
+                 int schedule, int per_wave, bool local, bool persistent, void *ws, size_t ws_bytes,
+                 hipStream_t stream)
 {
     int st = check_moe_shape(shp, P);
     if (st != UA_OK) return st;
@@ -64,6 +76,13 @@ int experts_call(const void *x, const int32_t *row_slot, const float *topk_w, co
     if (!aligned16(x) || !aligned16(topk_w) || !aligned16(row_slot) || !aligned16(W1) || !aligned16(W2) ||
         !aligned16(out) || !aligned16(act))
         return UA_ERR_ALIGN;
+    if (persistent) {
+        const int64_t words = ws_words(offsets, E_l, per_wave);
+        if (words < 0) return UA_ERR_UNSUPPORTED;
+        if (!ws) return UA_ERR_NULL;
+        if (!aligned16(ws)) return UA_ERR_ALIGN;
+        if (ws_bytes < (size_t)words * 4) return UA_ERR_WORKSPACE;
+    }
     moe::Problem p;
     p.x = (const uint16_t *)x;
     p.row_slot = row_slot;
@@ -77,7 +96,8 @@ int experts_call(const void *x, const int32_t *row_slot, const float *topk_w, co
     p.hidden = shp->hidden;
     p.inter = shp->inter;
     p.k = shp->k;
-    const hipError_t e = moe::launch_moe(p, schedule, per_wave, local, stream);
+    const hipError_t e = persistent ? moe::launch_moe_persist(p, schedule, per_wave, local, (unsigned *)ws, stream)
+                                    : moe::launch_moe(p, schedule, per_wave, local, stream);
     return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
@@ -118,7 +138,7 @@ int moe_experts_combine(const void *x, const int32_t *row_slot, const float *top
                         hipStream_t stream)
 {
     return experts_call(x, row_slot, topk_w, expert_offsets, W1, W2, P, shp, combine, act, schedule,
-                        experts_per_wave, false, stream);
+                        experts_per_wave, false, false, nullptr, 0, stream);
 }
 
 int moe_experts_local(const void *x, const int32_t *row_slot, const float *topk_w, const int64_t *expert_offsets,
@@ -126,7 +146,33 @@ int moe_experts_local(const void *x, const int32_t *row_slot, const float *topk_
                       int experts_per_wave, hipStream_t stream)
 {
     return experts_call(x, row_slot, topk_w, expert_offsets, W1, W2, P, shp, y_local, act, MOE_EXPERT_WAVE,
-                        experts_per_wave, true, stream);
+                        experts_per_wave, true, false, nullptr, 0, stream);
+}
+
+size_t moe_workspace_bytes(int P, const moe_shape *shp)
+{
+    if (check_moe_shape(shp, P) != UA_OK) return 0;
+    // token tiles of any layout: at most N / 256 + E_l with N <= P*T*k
+    const int64_t E_l = shp->E / P, n = moe::kWsHeader + (P * shp->T * shp->k) / 256 + E_l;
+    return (size_t)(((n * 4 + 255) / 256) * 256);
+}
+
+int moe_experts_combine_ws(const void *x, const int32_t *row_slot, const float *topk_w,
+                           const int64_t *expert_offsets, const void *W1, const void *W2, int P,
+                           const moe_shape *shp, void *combine, void *act, int schedule, int experts_per_wave,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return experts_call(x, row_slot, topk_w, expert_offsets, W1, W2, P, shp, combine, act, schedule,
+                        experts_per_wave, false, true, workspace, workspace_bytes, stream);
+}
+
+int moe_experts_local_ws(const void *x, const int32_t *row_slot, const float *topk_w,
+                         const int64_t *expert_offsets, const void *W1, const void *W2, int P,
+                         const moe_shape *shp, void *y_local, void *act, int experts_per_wave, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream)
+{
+    return experts_call(x, row_slot, topk_w, expert_offsets, W1, W2, P, shp, y_local, act, MOE_EXPERT_WAVE,
+                        experts_per_wave, true, true, workspace, workspace_bytes, stream);
 }
 
 int moe_combine_scatter(const void *y_local, const int32_t *row_slot, int64_t N, int P, const moe_shape *shp,

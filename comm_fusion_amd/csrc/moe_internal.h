@@ -31,6 +31,19 @@ struct Problem {
 // Expert-Wave order).
 hipError_t launch_moe(const Problem &p, int schedule, int per_wave, bool local, hipStream_t stream);
 
+// The persistent form: the same tiles and arithmetic in one launch per
+// kMaxWave experts, workgroups taking tiles in schedule order from a device
+// queue, each Linear-2 tile waiting for its token tile's Linear-1 tiles.
+// `ws` (device, 4-byte words): kWsHeader words of queue counters (one per
+// launch) and the timeout count, then one word per token tile
+// (token_tiles); the launch clears them first.
+constexpr int kMaxLaunches = 32;  // launches of one call: one queue counter each
+constexpr int kWsTimeouts = 32;   // header word counting bounded waits that gave up
+constexpr int kWsHeader = 64;
+int64_t token_tiles(const int64_t *offsets, int64_t E_l);
+hipError_t launch_moe_persist(const Problem &p, int schedule, int per_wave, bool local, unsigned *ws,
+                              hipStream_t stream);
+
 // Bit copy of y_local rows into their Combine slots.
 hipError_t launch_scatter(const uint16_t *y_local, const int32_t *row_slot, int64_t N, int64_t hidden,
                           uint16_t *combine, hipStream_t stream);

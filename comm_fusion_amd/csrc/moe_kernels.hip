@@ -35,8 +35,10 @@
 #include "moe_internal.h"
 #include "ua_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 namespace moe {
 namespace {
@@ -75,7 +77,8 @@ struct Seg {
     int32_t rows;    // its receive rows
     int32_t mtiles;  // token tiles, ceil(rows / BM)
     int32_t ntiles;  // feature tiles
-    int32_t tile0;   // first tile of the segment among its kind's tiles in the launch
+    int32_t tile0;   // first tile of the segment among its kind's tiles in the launch (or phase)
+    int32_t tt0;     // its first token tile among the call's token tiles (persistent form)
 };
 
 struct MoeArgs {
@@ -116,12 +119,17 @@ __device__ __forceinline__ u32x4 lds_read(unsigned addr)
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
     return r;
 }
-template <int N>
+template <int N, int NB>
 __device__ __forceinline__ void lgkm_wait(u32x4 (&fa)[4], u32x4 (&fb)[2])
 {
-    asm volatile("s_waitcnt lgkmcnt(%6)"
-                 : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1])
-                 : "i"(N));
+    if constexpr (NB > 1)
+        asm volatile("s_waitcnt lgkmcnt(%6)"
+                     : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1])
+                     : "i"(N));
+    else
+        asm volatile("s_waitcnt lgkmcnt(%5)"
+                     : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0])
+                     : "i"(N));
 }
 
 // One output tile: 256 features x 256 token rows, K in steps of 64.
@@ -133,11 +141,18 @@ __device__ __forceinline__ void lgkm_wait(u32x4 (&fa)[4], u32x4 (&fb)[2])
 // of copy c lands at byte 1024 c + 16 L: row 8 c + L / 8, position L % 8,
 // fetching chunk (L % 8) ^ (4 (c % 2) + L / 16)): as step s starts, the
 // token tile of step s+1 and then the weight tile of step s+2.  Wave (wf, wt)
-// computes features 128 wf .. +127 (four 32-row blocks) of token rows
-// 64 wt .. +63 (two).
-template <int KIND>
+// computes features 128 wf .. +127 (four 32-row blocks) of the token blocks
+// wt and wt + 4 (rows 32 wt .. +31 and 128 + 32 wt .. +31), so that the
+// rows of a partial tile (an expert's last) spread over all waves.  A token
+// block that lies wholly past the expert's rows is skipped: no fragment
+// reads, no MFMAs (and no copies of its rows).
+template <int KIND, bool COH>
 __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int n, lds_u8 *lds)
 {
+    // COH: act rows (Linear-2's token operand) are read at device scope
+    // (sc1), past any copy of them in this XCD's L2: in the persistent form
+    // they were written by other workgroups of the same launch.
+    constexpr int XAUX = KIND == 1 && COH ? 16 : 0;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wf = wave & 1, wt = wave >> 1;
@@ -147,6 +162,10 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     const char *wbase = (const char *)(KIND == 0 ? a.w1 + (int64_t)sg.expert * 2 * a.inter * a.hidden
                                                  : a.w2 + (int64_t)sg.expert * a.hidden * a.inter);
     const char *bbase = (const char *)(KIND == 0 ? a.x : a.act);
+    // rows of this tile inside the expert; this wave's token blocks among them
+    const int vrows = min(BM, sg.rows - m * BM);
+    const int nb = (32 * wt < vrows) + (128 + 32 * wt < vrows);
+    const bool xcopy = 32 * wave < vrows;  // this wave copies token rows 32 wave .. +31
 
     // This wave's copies: numbers NCPW wave .. of each operand tile.
     static_assert(NCPW % 2 == 0, "copy parity is the copy index's parity");
@@ -179,11 +198,12 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
             __builtin_amdgcn_global_load_lds((gbl_void *)(wbase + aoff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
     };
     auto copy_x = [&](int s, int x) {
+        if (!xcopy) return;
         const unsigned ko = (unsigned)s * BK * 2;
         lds_u8 *dst = lds + (NSTAGE_W + x) * TILE + NCPW * wave * 1024;
 #pragma unroll
         for (int i = 0; i < NCPW; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, XAUX);
     };
 
     // Per-lane LDS addresses of the fragment reads, one per k-substep KK
@@ -193,7 +213,7 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     const unsigned lbase = (unsigned)(uintptr_t)lds;
     const unsigned sw = (unsigned)((l32 >> 1) & 7);
     const unsigned ra = lbase + (unsigned)(128 * wf + l32) * 128;
-    const unsigned rb = lbase + NSTAGE_W * TILE + (unsigned)(64 * wt + l32) * 128;
+    const unsigned rb = lbase + NSTAGE_W * TILE + (unsigned)(32 * wt + l32) * 128;
     // weight stage 2 through its own bases (offset past the 16-bit field)
     unsigned pa[4], pa2[4], pb[4];
 #pragma unroll
@@ -215,10 +235,10 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     // the MFMAs of another set were issued after its own, which have
     // therefore started and taken their operands.
     u32x4 fa[3][4], fbr[3][2];
-    // the six fragment reads of k-substep KK of weight stage WS and token
-    // stage XS into set SET
-    auto reads = [&](auto wsc, auto xsc, auto kkc, auto setc) {
-        constexpr int WS = decltype(wsc)::value, XS = decltype(xsc)::value;
+    // the fragment reads of k-substep KK of weight stage WS and token stage
+    // XS into set SET: four weight blocks and this wave's NB token blocks
+    auto reads = [&](auto nbc, auto wsc, auto xsc, auto kkc, auto setc) {
+        constexpr int NB = decltype(nbc)::value, WS = decltype(wsc)::value, XS = decltype(xsc)::value;
         constexpr int KK = decltype(kkc)::value, SET = decltype(setc)::value;
         constexpr int OA = (WS & 1) * TILE, OB = XS * TILE;
         const unsigned p = WS == 2 ? pa2[KK] : pa[KK];
@@ -228,14 +248,15 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         da[1] = lds_read<OA + 1 * 4096>(p);
         da[2] = lds_read<OA + 2 * 4096>(p);
         da[3] = lds_read<OA + 3 * 4096>(p);
-        db[0] = lds_read<OB + 0 * 4096>(pb[KK]);
-        db[1] = lds_read<OB + 1 * 4096>(pb[KK]);
+        db[0] = lds_read<OB>(pb[KK]);
+        if constexpr (NB > 1) db[1] = lds_read<OB + 128 * 128>(pb[KK]);
     };
-    auto mfmas = [&](u32x4 (&da)[4], u32x4 (&db)[2]) {
+    auto mfmas = [&](auto nbc, u32x4 (&da)[4], u32x4 (&db)[2]) {
+        constexpr int NB = decltype(nbc)::value;
 #pragma unroll
         for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < NB; ++tb)
                 acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, da[fb]), __builtin_bit_cast(bf16x8, db[tb]), acc[fb][tb], 0, 0, 0);
     };
@@ -247,8 +268,11 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     // token tile of step s+1 and the weight tile of step s+2.  Each
     // substep's reads are issued before the previous substep's MFMAs; all
     // are waited for within the step.  PH = s % 3 also picks the fragment
-    // register sets (substep 4 s + j uses set (PH + j) % 3).
-    auto step = [&](int s, auto xsc, auto phc) {
+    // register sets (substep 4 s + j uses set (PH + j) % 3).  NB: this
+    // wave's token blocks inside the expert (a wave with none still copies
+    // and meets every barrier).
+    auto step = [&](auto nbc, int s, auto xsc, auto phc) {
+        constexpr int NB = decltype(nbc)::value, NR = 4 + NB;  // reads per substep
         constexpr int XS = decltype(xsc)::value, PH = decltype(phc)::value;
         using WS = std::integral_constant<int, PH>;
         constexpr int A = PH % 3, B = (PH + 1) % 3, C = (PH + 2) % 3;  // sets of substeps 0 (and 3), 1, 2
@@ -265,22 +289,24 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
             asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
         if (s + 1 < nk) copy_x(s + 1, XS ^ 1);
         if (s + 2 < nk) copy_w(s + 2, (PH + 2) % 3);
-        reads(WS(), xsc, K0(), SA());
-        reads(WS(), xsc, K1(), SB());
-        lgkm_wait<6>(fa[A], fbr[A]);
-        mfmas(fa[A], fbr[A]);
-        __builtin_amdgcn_sched_barrier(0);
-        reads(WS(), xsc, K2(), SC());
-        lgkm_wait<6>(fa[B], fbr[B]);
-        mfmas(fa[B], fbr[B]);
-        __builtin_amdgcn_sched_barrier(0);
-        reads(WS(), xsc, K3(), SA());
-        lgkm_wait<6>(fa[C], fbr[C]);
-        mfmas(fa[C], fbr[C]);
-        __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait<0>(fa[A], fbr[A]);
-        mfmas(fa[A], fbr[A]);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (NB > 0) {
+            reads(nbc, WS(), xsc, K0(), SA());
+            reads(nbc, WS(), xsc, K1(), SB());
+            lgkm_wait<NR, NB>(fa[A], fbr[A]);
+            mfmas(nbc, fa[A], fbr[A]);
+            __builtin_amdgcn_sched_barrier(0);
+            reads(nbc, WS(), xsc, K2(), SC());
+            lgkm_wait<NR, NB>(fa[B], fbr[B]);
+            mfmas(nbc, fa[B], fbr[B]);
+            __builtin_amdgcn_sched_barrier(0);
+            reads(nbc, WS(), xsc, K3(), SA());
+            lgkm_wait<NR, NB>(fa[C], fbr[C]);
+            mfmas(nbc, fa[C], fbr[C]);
+            __builtin_amdgcn_sched_barrier(0);
+            lgkm_wait<0, NB>(fa[A], fbr[A]);
+            mfmas(nbc, fa[A], fbr[A]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // prologue: the weight and token tiles of step 0, the weight tile of
@@ -294,23 +320,31 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     using P2 = std::integral_constant<int, 2>;
-    int s = 0;
-    for (; s + 6 <= nk; s += 6) {
-        step(s, S0(), P0());
-        step(s + 1, S1(), P1());
-        step(s + 2, S0(), P2());
-        step(s + 3, S1(), P0());
-        step(s + 4, S0(), P1());
-        step(s + 5, S1(), P2());
-    }
-    if (s < nk) {
-        step(s, S0(), P0());
-        step(s + 1, S1(), P1());
-    }
-    if (s + 2 < nk) {
-        step(s + 2, S0(), P2());
-        step(s + 3, S1(), P0());
-    }
+    auto loop = [&](auto nbc) {
+        int s = 0;
+        for (; s + 6 <= nk; s += 6) {
+            step(nbc, s, S0(), P0());
+            step(nbc, s + 1, S1(), P1());
+            step(nbc, s + 2, S0(), P2());
+            step(nbc, s + 3, S1(), P0());
+            step(nbc, s + 4, S0(), P1());
+            step(nbc, s + 5, S1(), P2());
+        }
+        if (s < nk) {
+            step(nbc, s, S0(), P0());
+            step(nbc, s + 1, S1(), P1());
+        }
+        if (s + 2 < nk) {
+            step(nbc, s + 2, S0(), P2());
+            step(nbc, s + 3, S1(), P0());
+        }
+    };
+    if (nb == 2)
+        loop(std::integral_constant<int, 2>());
+    else if (nb == 1)
+        loop(std::integral_constant<int, 1>());
+    else
+        loop(std::integral_constant<int, 0>());
     // every wave is done with the operand tiles (the Linear-2 epilogue reuses the LDS)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -320,7 +354,7 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         // SiLU(gate) * up -> act[row][128 n + 64 wf + ...], bf16
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const int rl = m * BM + 64 * wt + 32 * tb + l32;
+            const int rl = m * BM + 32 * (wt + 4 * tb) + l32;
             if (rl >= sg.rows) continue;
             uint16_t *dst = a.act + (int64_t)(sg.row0 + rl) * a.inter + L1_COLS * n + 64 * wf + 4 * g;
 #pragma unroll
@@ -343,12 +377,12 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         float wrow[2];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const int rl = m * BM + 64 * wt + 32 * tb + l32;
+            const int rl = m * BM + 32 * (wt + 4 * tb) + l32;
             wrow[tb] = rl < sg.rows ? a.topk_w[a.row_slot[sg.row0 + rl]] : 0.f;
         }
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const int tr = 64 * wt + 32 * tb + l32;
+            const int tr = 32 * (wt + 4 * tb) + l32;
 #pragma unroll
             for (int fb = 0; fb < 4; ++fb)
 #pragma unroll
@@ -413,9 +447,109 @@ void moe_tiles(MoeArgs a)
     const int t = idx - sg.tile0;
     const int nn = t / sg.mtiles, mm = t - nn * sg.mtiles;
     if (kind == 0)
-        tile<0>(a, sg, mm, nn, lds);
+        tile<0, false>(a, sg, mm, nn, lds);
     else
-        tile<1>(a, sg, mm, nn, lds);
+        tile<1, false>(a, sg, mm, nn, lds);
+}
+
+// ---- persistent form: one launch runs the whole schedule.  The schedule is
+// a sequence of phases (Expert-Wave: Linear-1 of wave 0, Linear-2 of wave 0,
+// Linear-1 of wave 1, ...; interleaved: Linear-1 of wave 0, then Linear-2 of
+// wave w-1 dealt between Linear-1 of wave w, ..., then the last Linear-2),
+// each dealt like one launch above.  Workgroups take queue positions in
+// order from one device counter, so long and short tiles pack over the CUs
+// as they free up instead of ending at each launch's tail.  (One queue per
+// XCD, each taking its XCD's run of every phase as the launch form maps
+// blocks, kept token tiles that share a weight slice in one L2 but ran
+// slower: a phase then ends at different times on different XCDs, and the
+// Linear-2 tiles of the next wait for the slowest.)  A Linear-2 tile
+// waits until all Linear-1 tiles of its token tile have stored their act
+// rows: each Linear-1 tile counts itself (release add) once every wave's
+// stores are complete; the Linear-2 tile's thread 0 polls the count at
+// device scope, bounded, and the tile then reads act at device scope.  The
+// Linear-1 tiles a Linear-2 tile waits for sit earlier in the queue, were
+// taken by running workgroups, and never wait themselves, so the waits end.
+
+struct Phase {
+    int32_t start;               // first queue position of the phase
+    int32_t seg_begin, seg_end;  // its segments in PersistArgs::m.seg
+    int32_t n_l1, n_l2;          // tiles of each kind in the phase
+};
+
+constexpr int kMaxPhase = 2 * kMaxWave + 1;
+constexpr unsigned kSpinLimit = 1u << 20;  // polls of a ready count before giving up
+
+struct PersistArgs {
+    MoeArgs m;          // operands and the segments of every phase
+    Phase ph[kMaxPhase];
+    int32_t nph;
+    int32_t n_tiles;    // queue positions
+    uint32_t l1_cols;   // Linear-1 tiles per token tile (inter / 128): the count a Linear-2 tile waits for
+    unsigned *queue;    // this launch's position counter (zero at the start)
+    unsigned *timeouts; // bounded waits that gave up (stays zero)
+    unsigned *ready;    // per token tile: Linear-1 tiles done
+};
+
+static_assert(sizeof(PersistArgs) <= 4096, "kernel arguments");
+
+__global__ __launch_bounds__(256) void clear_words(unsigned *p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+void moe_persist(PersistArgs a)
+{
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_all[LDS_BYTES];
+    lds_u8 *const lds = (lds_u8 *)lds_all;
+    typedef __attribute__((address_space(3))) int lds_i32;
+    lds_i32 *const pos_slot = (lds_i32 *)lds_all;
+    for (;;) {
+        __syncthreads();  // every wave is done with the previous tile's LDS
+        if (threadIdx.x == 0) *pos_slot = (int)atomicAdd(a.queue, 1u);
+        __syncthreads();
+        const int t = __builtin_amdgcn_readfirstlane(*pos_slot);  // uniform: the decode below stays scalar
+        __syncthreads();  // read by every wave before the tile's copies land
+        if (t >= a.n_tiles) return;
+        int k = 0;
+        while (k + 1 < a.nph && a.ph[k + 1].start <= t) ++k;
+        const Phase ph = a.ph[k];
+        const int64_t N = (int64_t)ph.n_l1 + ph.n_l2, b = t - ph.start;
+        const int64_t c2 = b * ph.n_l2 / N, c2n = (b + 1) * ph.n_l2 / N;
+        const int kind = c2n > c2 ? 1 : 0;
+        const int idx = kind ? (int)c2 : (int)(b - c2);
+        int si = ph.seg_begin;
+        for (int i = ph.seg_begin; i < ph.seg_end; ++i) {
+            const Seg &s = a.m.seg[i];
+            if (s.kind == kind && idx >= s.tile0 && idx < s.tile0 + s.mtiles * s.ntiles) si = i;
+        }
+        const Seg sg = a.m.seg[si];
+        const int tt = idx - sg.tile0;
+        const int nn = tt / sg.mtiles, mm = tt - nn * sg.mtiles;
+        const int rci = sg.tt0 + mm;  // this token tile's ready count
+        if (kind == 0) {
+            tile<0, true>(a.m, sg, mm, nn, lds);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's act stores are complete
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(a.ready + rci, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            unsigned *const rc = a.ready + rci;
+            if (threadIdx.x == 0) {
+                for (unsigned it = 0; __hip_atomic_load(rc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.l1_cols;
+                     ++it) {
+                    if (it >= kSpinLimit) {
+                        atomicAdd(a.timeouts, 1u);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();  // the act reads follow thread 0's observation of the count
+            tile<1, true>(a.m, sg, mm, nn, lds);
+        }
+    }
 }
 
 // Serial Combine: one 16-byte chunk per thread, row i of y_local to slot
@@ -430,12 +564,13 @@ __global__ __launch_bounds__(256) void scatter_rows(const uint16_t *src, const i
     *(u32x4 *)(dst + ((int64_t)row_slot[row] * chunks_per_row + w) * 8) = *(const u32x4 *)(src + c * 8);
 }
 
-// Append expert e's tiles of `kind` to a launch.
-void add_seg(MoeArgs &a, const Problem &p, int e, int kind)
+// Append expert e's tiles of `kind` to a launch (or a phase).
+void add_seg(MoeArgs &a, const Problem &p, int e, int kind, int32_t tt0 = 0)
 {
     const int64_t rows = p.offsets[e + 1] - p.offsets[e];
     if (rows == 0) return;
     Seg &s = a.seg[a.nseg++];
+    s.tt0 = tt0;
     s.kind = kind;
     s.expert = e;
     s.row0 = (int32_t)p.offsets[e];
@@ -489,6 +624,99 @@ hipError_t launch_moe(const Problem &p, int schedule, int per_wave, bool local, 
         }
     }
     return e;
+}
+
+int64_t token_tiles(const int64_t *offsets, int64_t E_l)
+{
+    int64_t n = 0;
+    for (int64_t e = 0; e < E_l; ++e) n += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+    return n;
+}
+
+hipError_t launch_moe_persist(const Problem &p, int schedule, int per_wave, bool local, unsigned *ws,
+                              hipStream_t stream)
+{
+    // workspace: [0, kWsHeader) queue counters (one per launch) and the
+    // timeout count, then one ready count per token tile; cleared first
+    const int64_t n_tt = token_tiles(p.offsets, p.E_l);
+    const int n_words = (int)(kWsHeader + n_tt);
+    {
+        unsigned *q = ws;
+        int n = n_words;
+        void *args[] = {(void *)&q, &n};
+        const hipError_t e = hipLaunchKernel((const void *)clear_words, dim3((unsigned)((n + 255) / 256)), dim3(256),
+                                             args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    PersistArgs a = {};
+    a.m.k = (int32_t)p.k;
+    a.m.hidden = (int32_t)p.hidden;
+    a.m.inter = (int32_t)p.inter;
+    a.m.out_local = local ? 1 : 0;
+    a.m.n_xcd = ua::device_xcd_count();
+    a.m.x = p.x;
+    a.m.row_slot = p.row_slot;
+    a.m.topk_w = p.topk_w;
+    a.m.w1 = p.w1;
+    a.m.w2 = p.w2;
+    a.m.act = p.act;
+    a.m.out = p.out;
+    a.l1_cols = (uint32_t)(p.inter / L1_COLS);
+    a.timeouts = ws + kWsTimeouts;
+    a.ready = ws + kWsHeader;
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    std::vector<int32_t> tt0(p.E_l + 1, 0);
+    for (int64_t x = 0; x < p.E_l; ++x) tt0[x + 1] = tt0[x] + (int32_t)((p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM);
+    const bool inter = schedule == kInterleaved && !local;
+    // launches of whole waves, at most kMaxWave experts each (one segment per
+    // expert and kind)
+    const int waves_per_launch = kMaxWave / per_wave;
+    const int n_waves = (int)((p.E_l + per_wave - 1) / per_wave);
+    int q = 0;
+    for (int w0 = 0; w0 < n_waves; w0 += waves_per_launch, ++q) {
+        const int w1 = std::min(n_waves, w0 + waves_per_launch);
+        a.m.nseg = 0;
+        a.nph = 0;
+        int32_t pos = 0;
+        // one phase: Linear-2 of wave l2w (or -1), Linear-1 of wave l1w (or -1)
+        auto phase = [&](int l1w, int l2w) {
+            Phase &ph = a.ph[a.nph];
+            ph.start = pos;
+            ph.seg_begin = a.m.nseg;
+            a.m.n_l1 = a.m.n_l2 = 0;
+            if (l2w >= 0)
+                for (int x = l2w * per_wave; x < (l2w + 1) * per_wave && x < p.E_l; ++x) add_seg(a.m, p, x, 1, tt0[x]);
+            if (l1w >= 0)
+                for (int x = l1w * per_wave; x < (l1w + 1) * per_wave && x < p.E_l; ++x) add_seg(a.m, p, x, 0, tt0[x]);
+            ph.seg_end = a.m.nseg;
+            ph.n_l1 = a.m.n_l1;
+            ph.n_l2 = a.m.n_l2;
+            if (ph.n_l1 + ph.n_l2 == 0) return;
+            pos += ph.n_l1 + ph.n_l2;
+            ++a.nph;
+        };
+        if (inter) {
+            phase(w0, -1);
+            for (int w = w0 + 1; w < w1; ++w) phase(w, w - 1);
+            phase(-1, w1 - 1);
+        } else {
+            for (int w = w0; w < w1; ++w) {
+                phase(w, -1);
+                phase(-1, w);
+            }
+        }
+        if (pos == 0) continue;
+        a.n_tiles = pos;
+        a.queue = ws + q;
+        const unsigned grid = (unsigned)std::min<int64_t>(pos, n_cu > 0 ? n_cu : 1);
+        void *args[] = {&a};
+        e = hipLaunchKernel((const void *)moe_persist, dim3(grid), dim3(NT), args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_scatter(const uint16_t *y_local, const int32_t *row_slot, int64_t N, int64_t hidden,

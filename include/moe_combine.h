@@ -41,7 +41,8 @@
  * allocates nothing.  Calls are asynchronous on `stream` (a hipStream_t of
  * the device holding the buffers; NULL = its default stream).
  * Errors: status codes of ulysses_attn.h (UA_OK, UA_ERR_NULL,
- * UA_ERR_SHAPE, UA_ERR_ALIGN, UA_ERR_UNSUPPORTED, UA_ERR_HIP); arguments are
+ * UA_ERR_SHAPE, UA_ERR_ALIGN, UA_ERR_UNSUPPORTED, UA_ERR_HIP,
+ * UA_ERR_WORKSPACE); arguments are
  * validated on the host before any device access.  row_slot entries are
  * not read on the host: each must be < P*T*k and name a slot whose expert is
  * the row's (moe_recv_layout produces exactly such rows).
@@ -100,6 +101,35 @@ int moe_experts_combine(const void *x, const int32_t *row_slot, const float *top
                         int experts_per_wave, hipStream_t stream);
 
 /*
+ * Workspace of the persistent form (below) for any call with this shape:
+ * bytes of device memory, a multiple of 256 (0 for an invalid shape).
+ */
+size_t moe_workspace_bytes(int P, const moe_shape *shp);
+
+/*
+ * The fused path in its persistent form (the pages' MegaMoE runs the
+ * schedule inside one persistent kernel; arXiv abstract page, Abstract;
+ * pith.science review page, Fig. 4): the same tiles, arithmetic and outputs
+ * as moe_experts_combine (bit-identical), run by one launch per 32 local
+ * experts whose workgroups take the schedule's tiles in order from a device
+ * queue; a Linear-2 tile starts once every Linear-1 tile of its token rows
+ * has stored its act rows.  `workspace` (device, 16-byte aligned, at least
+ * moe_workspace_bytes(P, shp) bytes, else UA_ERR_WORKSPACE; NULL gives
+ * UA_ERR_NULL) holds the queue and the per-token-tile counts; the call
+ * clears it on `stream` first, so it needs no initialisation, and calls
+ * that share one workspace must not overlap.  Word 32 of the workspace
+ * (as uint32) counts bounded waits that gave up (zero after every correct
+ * call).  More
+ * than 32 launches (more than 1024 local experts at 32 per wave) give
+ * UA_ERR_UNSUPPORTED.
+ */
+int moe_experts_combine_ws(const void *x, const int32_t *row_slot, const float *topk_w,
+                           const int64_t *expert_offsets, const void *W1, const void *W2, int P,
+                           const moe_shape *shp, void *combine, void *act, int schedule,
+                           int experts_per_wave, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Serial baseline, expert half: the same computation with Linear-2 writing
  * row i's weighted output to y_local [N][hidden] (row i of the receive
  * layout) instead of its Combine slot (Expert-Wave order).
@@ -108,6 +138,13 @@ int moe_experts_local(const void *x, const int32_t *row_slot, const float *topk_
                       const int64_t *expert_offsets, const void *W1, const void *W2, int P,
                       const moe_shape *shp, void *y_local, void *act, int experts_per_wave,
                       hipStream_t stream);
+
+/* moe_experts_local in the persistent form (Expert-Wave order; workspace as
+ * for moe_experts_combine_ws). */
+int moe_experts_local_ws(const void *x, const int32_t *row_slot, const float *topk_w,
+                         const int64_t *expert_offsets, const void *W1, const void *W2, int P,
+                         const moe_shape *shp, void *y_local, void *act, int experts_per_wave,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Serial baseline, exchange half: copies row i of y_local [N][hidden]

@@ -110,10 +110,11 @@ def test_key_split_call_replays_from_a_graph():
 
 
 def test_moe_experts_combine_replays_from_a_graph():
-    """The MoE path (several launches per call, both schedules) inside a
-    graph: every replay bit-equal to the eager call; routing weights doubled
-    in place (exact in fp32, and the weighted output is rounded once) show up
-    in the next replay."""
+    """The MoE path (several launches per call, both schedules, and the
+    persistent form with its workspace clear) inside a graph: every replay
+    bit-equal to the eager call, with the workspace refilled with garbage
+    between replays; routing weights doubled in place (exact in fp32, and the
+    weighted output is rounded once) show up in the next replay."""
     import torch
     from moe_inputs import MOE_SENTINEL_BITS, MOE_WORKLOADS, moe_tensors
     w = MOE_WORKLOADS["moe_small_skewed"]
@@ -126,18 +127,23 @@ def test_moe_experts_combine_replays_from_a_graph():
     act = torch.empty(N * w.inter, dtype=torch.bfloat16, device="cuda")
     sentinel = MOE_SENTINEL_BITS - 0x10000 if MOE_SENTINEL_BITS >= 0x8000 else MOE_SENTINEL_BITS
     n_out = w.P * w.T * w.k * w.hidden
-    outs = [torch.full((n_out,), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16) for _ in range(2)]
+    outs = [torch.full((n_out,), sentinel, dtype=torch.int16, device="cuda").view(torch.bfloat16) for _ in range(3)]
+    ws = ua.new_moe_workspace(dx.view(w.P, w.T, w.hidden), dW1.view(w.E_l, 2 * w.inter, w.hidden), dtw, w.P, w.E)
+    ws.fill_(0xA5)
 
     def calls():
         ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, outs[0], act,
                                schedule=ua.MOE_INTERLEAVED, experts_per_wave=3)
         ua.moe_experts_combine(dx, drs, dtw, off, dW1, dW2, w.P, w.E, outs[1], act,
                                schedule=ua.MOE_EXPERT_WAVE, experts_per_wave=3)
+        ua.moe_experts_combine_ws(dx, drs, dtw, off, dW1, dW2, w.P, w.E, outs[2], act, ws,
+                                  schedule=ua.MOE_INTERLEAVED, experts_per_wave=3)
 
     calls()
     torch.cuda.synchronize()
     refs = [o.clone() for o in outs]
     assert torch.equal(refs[0].view(torch.int16), refs[1].view(torch.int16))
+    assert torch.equal(refs[0].view(torch.int16), refs[2].view(torch.int16))
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -152,11 +158,13 @@ def test_moe_experts_combine_replays_from_a_graph():
         for o in outs:
             o.view(torch.int16).fill_(sentinel)
         act.zero_()
+        ws.fill_(0xA5)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         for o, r in zip(outs, refs):
             assert torch.equal(o.view(torch.int16), r.view(torch.int16))
+        assert int(ws.view(torch.int32)[32]) == 0
 
     dtw.mul_(2)
     torch.cuda.synchronize()
@@ -168,3 +176,4 @@ def test_moe_experts_combine_replays_from_a_graph():
     ref = refs[0].view(-1, w.hidden)[served].float()
     assert torch.equal(got, ref * 2)
     assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16))
+    assert torch.equal(outs[2].view(torch.int16), outs[0].view(torch.int16))

@@ -118,3 +118,131 @@ def test_every_tile_is_dealt_once_and_kinds_interleave(n_l1, n_l2):
         c = np.concatenate([[0], np.cumsum(kinds)])
         b = np.arange(N + 1)
         assert np.all(np.abs(c - b * n_l2 / N) < 1.0)
+
+
+# ---- the persistent form's queue (restated from the launch and the kernel) ----
+
+MAX_WAVE = 32
+
+
+def _queue(n_e, G, interleaved, BM=256, l1_cols=16, l2_cols=28):
+    """Every queue position of every launch, decoded as the kernel does:
+    launches of whole waves of at most 32 experts; per launch, phases
+    (Expert-Wave: L1 w, L2 w, ...; interleaved: L1 w0, L2 w-1 + L1 w, ...,
+    L2 last), each phase dealt like a launch of the per-wave form.  Returns
+    [(launch, position, kind, expert, token tile, feature tile)]."""
+    E_l = len(n_e)
+    mt = [-(-int(n) // BM) for n in n_e]
+    n_waves = -(-E_l // G)
+    per_launch = MAX_WAVE // G
+    out = []
+    for q, w0 in enumerate(range(0, n_waves, per_launch)):
+        w1 = min(n_waves, w0 + per_launch)
+        phases = []
+
+        def phase(l1w, l2w):
+            segs = []
+            cnt = [0, 0]
+            for kind, w in ((1, l2w), (0, l1w)):
+                if w < 0:
+                    continue
+                for e in range(w * G, min((w + 1) * G, E_l)):
+                    if n_e[e] == 0:
+                        continue
+                    nt = l1_cols if kind == 0 else l2_cols
+                    segs.append((kind, e, cnt[kind], mt[e], nt))
+                    cnt[kind] += mt[e] * nt
+            if cnt[0] + cnt[1]:
+                phases.append((segs, cnt[0], cnt[1]))
+        if interleaved:
+            phase(w0, -1)
+            for w in range(w0 + 1, w1):
+                phase(w, w - 1)
+            phase(-1, w1 - 1)
+        else:
+            for w in range(w0, w1):
+                phase(w, -1)
+                phase(-1, w)
+        pos = 0
+        for segs, n1, n2 in phases:
+            N = n1 + n2
+            for b in range(N):
+                c2, c2n = b * n2 // N, (b + 1) * n2 // N
+                kind, idx = (1, c2) if c2n > c2 else (0, b - c2)
+                hit = [s for s in segs if s[0] == kind and s[2] <= idx < s[2] + s[3] * s[4]]
+                assert len(hit) == 1
+                _, e, t0, m_t, _ = hit[0]
+                nn, mm = divmod(idx - t0, m_t)
+                out.append((q, pos + b, kind, e, mm, nn))
+            pos += N
+    return out
+
+
+@pytest.mark.parametrize("G", [1, 3, 8, 32])
+@pytest.mark.parametrize("interleaved", [True, False])
+@pytest.mark.parametrize("n_e", [[455, 545, 0, 1, 256, 257, 512, 30] * 4, [600] * 70, [0, 0, 5]])
+def test_persistent_queue_deals_every_tile_once_after_its_dependencies(G, interleaved, n_e):
+    q = _queue(n_e, G, interleaved)
+    tiles = [(k, e, mm, nn) for _, _, k, e, mm, nn in q]
+    want = [(k, e, mm, nn) for e, n in enumerate(n_e) for mm in range(-(-n // 256))
+            for k, ncol in ((0, 16), (1, 28)) for nn in range(ncol)]
+    assert sorted(tiles) == sorted(want)
+    # a Linear-2 tile's 16 Linear-1 tiles come earlier in the same launch's
+    # queue (so the workgroups that took them are running and never wait)
+    where = {(k, e, mm, nn): (launch, pos) for launch, pos, k, e, mm, nn in q}
+    for launch, pos, k, e, mm, nn in q:
+        if k == 1:
+            for c in range(16):
+                lq, lp = where[(0, e, mm, c)]
+                assert lq == launch and lp < pos
+    # interleaved: in every launch but the first wave's, a phase holds both kinds
+    if interleaved and G < len(n_e):
+        kinds = {}
+        for launch, pos, k, *_ in q:
+            kinds.setdefault(launch, set()).add(k)
+        assert all(v == {0, 1} for v in kinds.values())
+
+
+def test_persistent_queue_catches_a_reversed_phase_order():
+    # a mutant that runs each wave's Linear-2 phase before its Linear-1 phase
+    # puts Linear-2 tiles ahead of their dependencies
+    q = _queue([300, 40], 1, False)
+    order = sorted(q, key=lambda r: (r[0], r[2] == 0, r[1]))  # kind 1 first
+    seen = set()
+    bad = False
+    for _, _, k, e, mm, nn in order:
+        if k == 1 and any((0, e, mm, c) not in seen for c in range(16)):
+            bad = True
+        seen.add((k, e, mm, nn))
+    assert bad
+
+
+def test_persistent_workspace_size_and_validation():
+    ok = MoeShape(64, 256, 128, 8, 2)
+    n = _lib().moe_workspace_bytes(2, ctypes.byref(ok))
+    # header of 64 words (a queue counter per launch, the timeout count) plus
+    # one word per token tile: N <= 2*64*2 = 256 rows over 4 local experts
+    # give at most 1 + 4 token tiles
+    assert n % 256 == 0 and n >= 4 * (64 + 5)
+    assert _lib().moe_workspace_bytes(2, ctypes.byref(MoeShape(64, 384, 128, 8, 2))) == 0
+    off = np.asarray([0, 3, 3, 10, 12], np.int64)
+    L = _lib()
+
+    def call(ws, nbytes, G=4):
+        return L.moe_experts_combine_ws(A, A, A, off.ctypes.data, A, A, 2, ctypes.byref(ok), A, A, 1, G, ws, nbytes,
+                                        None)
+    assert call(None, n) == ua.UA_ERR_NULL
+    assert call(A + 4, n) == ua.UA_ERR_ALIGN
+    assert call(A, 4 * 64) == ua.UA_ERR_WORKSPACE          # no room for the 4 token tiles
+    assert call(A, n, G=0) == ua.UA_ERR_UNSUPPORTED
+    assert L.moe_experts_local_ws(A, A, A, off.ctypes.data, A, A, 2, ctypes.byref(ok), A, A, 4, None, n,
+                                  None) == ua.UA_ERR_NULL
+    zero = np.zeros(5, np.int64)
+    assert L.moe_experts_combine_ws(0, 0, 0, zero.ctypes.data, 0, 0, 2, ctypes.byref(ok), 0, 0, 1, 4, None, 0,
+                                    None) == ua.UA_OK  # empty
+    # more than 32 launches: 1056 local experts at one per wave
+    big = MoeShape(1, 256, 128, 1056, 1)
+    boff = np.zeros(1057, np.int64)
+    boff[-1] = 1
+    assert L.moe_experts_combine_ws(A, A, A, boff.ctypes.data, A, A, 1, ctypes.byref(big), A, A, 1, 1, A, 1 << 20,
+                                    None) == ua.UA_ERR_UNSUPPORTED

@@ -12,7 +12,9 @@ receive rows), and checks for every tile of the five MoE workloads, of the
 ragged-expert case of the GPU tests and of shapes at the size limits that
 every 16-byte access lies inside its buffer and that no 32-bit offset wraps.
 A mutant that takes Linear-2's k length from hidden instead of inter is
-shown to read out of bounds.
+shown to read out of bounds.  For an expert's partial last tile, the waves
+that skip their token copies and their padded token blocks are checked to
+leave every row that is read copied and every valid row computed.
 """
 import numpy as np
 import pytest
@@ -163,3 +165,46 @@ def test_mutant_with_the_wrong_k_length_reads_out_of_bounds():
     off, slots = _layout(idx, w.rank, w.P, w.hidden, w.inter, w.E)
     bad = check_problem(w.P, w.T, w.hidden, w.inter, w.E, w.k, off, slots, k_len_l2=w.hidden)
     assert bad and all(b[1] == 1 for b in bad)
+
+
+def partial_tile_plan(vrows):
+    """Restates the kernel's partial-tile rule for a tile holding `vrows`
+    valid token rows: wave (wf, wt) = (wave % 2, wave // 2) computes token
+    blocks wt and wt + 4 (32 rows each) while they start below vrows; wave w
+    copies token rows 32 w .. 32 w + 31 only while 32 w < vrows.  Returns
+    (rows read by the fragment reads, rows copied, rows computed)."""
+    read, copied, computed = set(), set(), set()
+    for wave in range(NW):
+        wt = wave >> 1
+        nb = int(32 * wt < vrows) + int(128 + 32 * wt < vrows)
+        for tb in range(nb):                        # blocks wt, then wt + 4
+            rows = range(32 * (wt + 4 * tb), 32 * (wt + 4 * tb) + 32)
+            read.update(rows)
+            computed.update(rows)
+        if 32 * wave < vrows:
+            copied.update(range(32 * wave, 32 * wave + 32))
+    return read, copied, computed
+
+
+@pytest.mark.parametrize("vrows", list(range(1, BM + 1)))
+def test_partial_tiles_read_only_copied_rows_and_compute_every_row(vrows):
+    read, copied, computed = partial_tile_plan(vrows)
+    assert read <= copied
+    assert set(range(vrows)) <= computed
+    # padded blocks are skipped: at most the 31 rows past vrows that share
+    # the last valid block are computed
+    assert max(computed) < vrows + 31 and len(computed) == 32 * -(-vrows // 32)
+
+
+def test_partial_tile_plan_catches_a_wrong_block_map():
+    # the mapping before the interleave (blocks 2 wt, 2 wt + 1) with the
+    # same copy rule would leave valid rows uncomputed
+    def old(vrows):
+        computed = set()
+        for wave in range(NW):
+            wt = wave >> 1
+            nb = int(32 * wt < vrows) + int(128 + 32 * wt < vrows)
+            for tb in range(nb):
+                computed.update(range(64 * wt + 32 * tb, 64 * wt + 32 * tb + 32))
+        return computed
+    assert any(not set(range(v)) <= old(v) for v in range(1, BM + 1))
