@@ -19,7 +19,8 @@
 //  * outputs are computed transposed, C^T = W X^T: the weight rows are the A
 //    operand and the token rows the B operand, so every lane holds one token
 //    row and 16 of its features per block (runs of 4 consecutive features);
-//  * operand tiles go global -> LDS directly (no VGPR staging): weight tiles
+//  * operand tiles go global -> LDS directly (buffer loads into the LDS, no
+//    VGPR staging, no vector instruction per copy): weight tiles
 //    (mostly from HBM) through three stages, copied two k-steps ahead, token
 //    tiles (mostly L2 hits) through two, one step ahead; one barrier per
 //    step of 32 MFMAs per wave; the operand reads are explicit LDS
@@ -66,8 +67,9 @@ constexpr int NCPW = TILE / 1024 / NW;  // 1 KiB copies per wave per operand til
 constexpr int L1_COLS = 128;            // intermediate columns per Linear-1 tile
 constexpr int L2_COLS = 256;            // hidden columns per Linear-2 tile
 
-typedef const __attribute__((address_space(1))) void gbl_void;
 typedef __attribute__((address_space(3))) void lds_void;
+// word 3 of a raw buffer descriptor (gfx9: 32-bit data format, no swizzle)
+constexpr int kBufferFlags = 0x00020000;
 
 // One expert's tiles of one kind in a launch.
 struct Seg {
@@ -190,20 +192,25 @@ __device__ __forceinline__ void tile(const MoeArgs &a, const Seg &sg, int m, int
         boff[i] = brow * (unsigned)K * 2 + chunk16;
     }
     // weight tile of step s into weight stage w; token tile into token stage x
+    // Buffer loads into the LDS: the operand's base in a descriptor, the
+    // lane's 32-bit offset, and the step's k offset as the scalar offset, so
+    // a copy costs no vector instruction.  The descriptor's range is the
+    // whole 32-bit offset space (no clipping): the host keeps every offset
+    // of an operand below 2^32.
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc((void *)wbase, (short)0, -1, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc((void *)bbase, (short)0, -1, kBufferFlags);
     auto copy_w = [&](int s, int w) {
-        const unsigned ko = (unsigned)s * BK * 2;
         lds_u8 *dst = lds + w * TILE + NCPW * wave * 1024;
 #pragma unroll
         for (int i = 0; i < NCPW; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void *)(wbase + aoff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void *)(dst + i * 1024), 16, aoff[i], s * BK * 2, 0, 0);
     };
     auto copy_x = [&](int s, int x) {
         if (!xcopy) return;
-        const unsigned ko = (unsigned)s * BK * 2;
         lds_u8 *dst = lds + (NSTAGE_W + x) * TILE + NCPW * wave * 1024;
 #pragma unroll
         for (int i = 0; i < NCPW; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_void *)(bbase + boff[i] + ko), (lds_void *)(dst + i * 1024), 16, 0, XAUX);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_void *)(dst + i * 1024), 16, boff[i], s * BK * 2, 0, XAUX);
     };
 
     // Per-lane LDS addresses of the fragment reads, one per k-substep KK
