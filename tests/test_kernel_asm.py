@@ -366,6 +366,117 @@ def test_spill_lane_check_sees_a_spill_in_a_k_loop():
     assert spill_lanes_in_inner_loops(lines[:3]) == []
 
 
+# ---- the persistent MoE kernel's hand-off of act rows ----
+#
+# A Linear-1 tile stores its act rows from every wave (plain stores), each
+# wave waits for its own stores (s_waitcnt vmcnt(0)), a workgroup barrier
+# follows, then thread 0's device-scope release add (buffer_wbl2, then the
+# atomic) counts the tile; Linear-2 tiles of other workgroups read those rows
+# once the count is complete.  The release's own wait covers only thread 0's
+# wave, so no barrier from which a release add is reached may be passed with
+# a store of the wave still in flight.
+
+def _is_store(line: str) -> bool:
+    return line.split(None, 1)[0].startswith(("global_store", "buffer_store", "flat_store"))
+
+
+def _is_release_add(block, j):
+    """global_atomic_add at position j of the block with a buffer_wbl2 before
+    it in the same block (the compiler's release sequence)."""
+    op = block[j][1].split(None, 1)[0]
+    return op.startswith("global_atomic_add") and any(l.startswith("buffer_wbl2") for _, l in block[:j])
+
+
+def barriers_before_a_release_with_stores_in_flight(lines):
+    blocks, succ = _blocks(lines)
+    n = len(blocks)
+    # forward: a store of this wave may be outstanding (no vmcnt(0) since)
+    inn = [None] * n
+    inn[0] = False
+    work = [0]
+
+    def step(st, line):
+        op = line.split(None, 1)[0]
+        if op.startswith("s_waitcnt"):
+            m = _VM.search(line)
+            return False if (m and int(m.group(1)) == 0) else st
+        return True if _is_store(line) else st
+    while work:
+        k = work.pop()
+        st = inn[k]
+        for _, line in blocks[k]:
+            st = step(st, line)
+        for t in succ[k]:
+            m = st if inn[t] is None else (inn[t] or st)
+            if m != inn[t]:
+                inn[t] = m
+                work.append(t)
+    # backward: from the start of a block, a release add is reached before
+    # any barrier on some path
+    reach = [False] * n
+    changed = True
+    while changed:
+        changed = False
+        for k in range(n):
+            v = None
+            for j, (_, line) in enumerate(blocks[k]):
+                if _is_release_add(blocks[k], j):
+                    v = True
+                    break
+                if line.startswith("s_barrier"):
+                    v = False
+                    break
+            if v is None:
+                v = any(reach[t] for t in succ[k])
+            if v and not reach[k]:
+                reach[k] = changed = True
+    bad = []
+    for k in range(n):
+        st = bool(inn[k])
+        for j, (i, line) in enumerate(blocks[k]):
+            if line.startswith("s_barrier") and st:
+                lead = None
+                for jj in range(j + 1, len(blocks[k])):
+                    if _is_release_add(blocks[k], jj):
+                        lead = True
+                        break
+                    if blocks[k][jj][1].startswith("s_barrier"):
+                        lead = False
+                        break
+                if lead is None:
+                    lead = any(reach[t] for t in succ[k])
+                if lead:
+                    bad.append((i, line))
+            st = step(st, line)
+    return bad
+
+
+def test_persistent_moe_counts_a_tile_only_after_every_wave_stored_it():
+    bodies = {n: l for n, l in _kernel_bodies(build.assembly("moe_kernels.hip"), "moe_persist").items()}
+    assert len(bodies) == 1
+    for name, lines in bodies.items():
+        blocks, _ = _blocks(lines)
+        releases = [(k, j) for k, b in enumerate(blocks) for j in range(len(b)) if _is_release_add(b, j)]
+        assert releases, "no release add found in " + name
+        assert not barriers_before_a_release_with_stores_in_flight(lines)
+
+
+def test_release_checker_catches_a_barrier_before_the_stores_complete():
+    bad = ["global_store_dwordx2 v[0:1], v[2:3], off",
+           "s_waitcnt vmcnt(63) expcnt(7) lgkmcnt(15)",
+           "s_barrier",
+           "buffer_wbl2 sc1",
+           "s_waitcnt vmcnt(0)",
+           "global_atomic_add v1, v1, v66, s[2:3] sc1"]
+    assert barriers_before_a_release_with_stores_in_flight(bad) == [(2, "s_barrier")]
+    good = bad[:1] + ["s_waitcnt vmcnt(0)"] + bad[1:]
+    assert barriers_before_a_release_with_stores_in_flight(good) == []
+    # stores before a barrier that leads to no release (the Linear-2
+    # epilogue's Combine stores before the next tile's barrier) are fine
+    other = ["global_store_dwordx4 v[0:1], v[2:5], off", "s_barrier", "global_atomic_add v1, v1, v66, s[2:3]"]
+    assert barriers_before_a_release_with_stores_in_flight(other) == []
+
+
 def test_moe_lds_results_not_used_before_their_wait():
     # the MoE kernel reads its MFMA operands with the same explicit LDS reads
     bodies = {n: l for n, l in _kernel_bodies(build.assembly("moe_kernels.hip"), "moe_").items()
@@ -375,3 +486,16 @@ def test_moe_lds_results_not_used_before_their_wait():
         assert sum(l.startswith("ds_read_b128") for l in lines) >= 48, name
         bad = early_uses(lines)
         assert not bad, "%s: %s" % (name, bad[:5])
+
+
+def test_persistent_moe_reads_act_at_device_scope():
+    # the Linear-2 tiles of the persistent kernel copy act rows written by
+    # other workgroups of the same launch: those copies carry sc1 (read past
+    # the XCD's L2); the per-wave kernel reads act after a launch boundary
+    a = build.assembly("moe_kernels.hip")
+    persist = "\n".join(_raw_body(a, "moe_persist"))
+    tiles = "\n".join(_raw_body(a, "moe_tiles"))
+    lds_copies = re.compile(r"^\s*buffer_load_dwordx4\b.*\blds\b.*$", re.M)
+    p_sc1 = [l for l in lds_copies.findall(persist) if re.search(r"\bsc1\b", l)]
+    assert p_sc1, "no device-scope act copies in moe_persist"
+    assert not [l for l in lds_copies.findall(tiles) if re.search(r"\bsc1\b", l)]
