@@ -128,3 +128,19 @@ def test_persistent_full_size_alternating_inputs(name):
         got = _persist(c, sch, G, ws).view(torch.int16)
         assert torch.equal(got, refs[key]), "call %d: input %s, G %d, schedule %d" % (i, key, G, sch)
         assert _timeouts(ws) == 0
+
+
+@pytest.mark.parametrize("G", [3, 32])
+def test_persistent_form_over_several_launches(G):
+    # 80 local experts: at 3 experts per wave a launch holds 10 waves (30
+    # experts), at 32 one wave, so the call runs 3 launches, each with its
+    # own queue counter in the workspace
+    w = MoeWorkload("moe_many", P=2, rank=1, T=512, hidden=256, inter=128, E=160, k=4, seed=41)
+    c = Case(w)
+    ws = _ws(c)
+    print("moe persistent, %d local experts, G %d, N=%d" % (w.E_l, G, c.N), flush=True)
+    ref = _host_bits(c.fused(ua.MOE_INTERLEAVED, G))
+    _check_all(c, ref, "many experts, launch form")
+    for schedule in (ua.MOE_INTERLEAVED, ua.MOE_EXPERT_WAVE):
+        np.testing.assert_array_equal(_host_bits(_persist(c, schedule, G, ws)), ref)
+        assert _timeouts(ws) == 0
