@@ -473,7 +473,8 @@ void moe_tiles(MoeArgs a)
 // waits until all Linear-1 tiles of its token tile have stored their act
 // rows: each Linear-1 tile counts itself (release add) once every wave's
 // stores are complete; the Linear-2 tile's thread 0 polls the count at
-// device scope, bounded, and the tile then reads act at device scope.  The
+// device scope, bounded, then acquires, and the tile reads act at device
+// scope (sc1, past any line of it in this XCD's L2).  The
 // Linear-1 tiles a Linear-2 tile waits for sit earlier in the queue, were
 // taken by running workgroups, and never wait themselves, so the waits end.
 
@@ -552,8 +553,10 @@ void moe_persist(PersistArgs a)
                     }
                     __builtin_amdgcn_s_sleep(2);
                 }
+                // pairs with the Linear-1 tiles' release adds
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             }
-            __syncthreads();  // the act reads follow thread 0's observation of the count
+            __syncthreads();  // the act reads follow thread 0's acquire
             tile<1, true>(a.m, sg, mm, nn, lds);
         }
     }

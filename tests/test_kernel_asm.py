@@ -499,3 +499,5 @@ def test_persistent_moe_reads_act_at_device_scope():
     p_sc1 = [l for l in lds_copies.findall(persist) if re.search(r"\bsc1\b", l)]
     assert p_sc1, "no device-scope act copies in moe_persist"
     assert not [l for l in lds_copies.findall(tiles) if re.search(r"\bsc1\b", l)]
+    # thread 0's acquire after it observes the count (pairs with the release)
+    assert re.search(r"^\s*buffer_inv sc1\b", persist, re.M)
