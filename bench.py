@@ -272,24 +272,28 @@ def cpu_all(full_limit_s: float) -> dict:
     return {"kind": "oracle", "cores": threads, "timings": res}
 
 
-def traced_call(ua, torch, q, k, v, w, dest) -> dict:
-    """One call of the measurement build: per-work-unit epilogue store spans
-    (from every wave's rows ready to every wave's stores complete) and the
-    shader clock (cycles over the 100 MHz constant clock)."""
-    n = ua.work_units(w.B, w.S, w.H, w.d, w.P)
+def traced_call(ua, torch, q, k, v, w, dest, workspace=None) -> dict:
+    """One call of the measurement build of the timed launch (with the
+    workspace of a split launch, so its clock is read on that launch):
+    per-workgroup epilogue store spans (from every wave's rows ready to every
+    wave's stores complete) and the shader clock (cycles over the 100 MHz
+    constant clock)."""
+    n = ua.work_units(w.B, w.S, w.H, w.d, w.P, workspace=workspace is not None)
     trace = torch.zeros(4 * n, dtype=torch.int64, device=q.device)
-    ua.attn_ulysses_fused_trace(q, k, v, w.rank, w.P, dest, trace)
+    ua.attn_ulysses_fused_trace(q, k, v, w.rank, w.P, dest, trace, workspace=workspace)
     torch.cuda.synchronize()
     t = trace.cpu().numpy().reshape(n, 4).astype(np.float64)
+    # a split launch's parts merged elsewhere store nothing: [1] == [2]
     span_us = (t[:, 2] - t[:, 1]) / 100.0          # 100 MHz ticks -> us
     life_us = (t[:, 2] - t[:, 0]) / 100.0
-    unit_bytes = w.out_bytes / n                    # mean bytes a work unit stores
-    ok = span_us > 0
+    ok = span_us > 0                                # the workgroups that stored rows
+    unit_bytes = w.out_bytes / max(int(ok.sum()), 1)  # mean bytes a storing workgroup stores
     unit_mhz = t[:, 3] / np.maximum(life_us, 1e-3)   # cycles per us = MHz
+    sp = span_us[ok] if ok.any() else span_us
     return {
         "trace_work_units": n,
-        "epilogue_span_us_mean": round(float(span_us.mean()), 3),
-        "epilogue_span_us_p90": round(float(np.percentile(span_us, 90)), 3),
+        "epilogue_span_us_mean": round(float(sp.mean()), 3),
+        "epilogue_span_us_p90": round(float(np.percentile(sp, 90)), 3),
         "epilogue_unit_GBs_mean": round(float((unit_bytes / (span_us[ok] * 1e-6)).mean() / 1e9), 1) if ok.any() else None,
         "epilogue_share_of_unit_time": round(float(span_us.sum() / life_us.sum()), 4),
         "sclk_mhz_trace": round(float(t[:, 3].sum() / (life_us.sum() * 1e-6) / 1e6), 1),
@@ -408,7 +412,8 @@ class Case:
         torch.cuda.synchronize()
 
     def traced(self):
-        return traced_call(self.ua, self.torch, self.q, self.k, self.v, self.w, self.scratch_dest)
+        return traced_call(self.ua, self.torch, self.q, self.k, self.v, self.w, self.scratch_dest,
+                           self.ws if self.n_split > 1 else None)
 
     def measure(self, steps, warmup, rounds):
         """Warm-up (counted and timed), the traced clock, K fused launches back
@@ -455,6 +460,11 @@ class Case:
             "speedup_serial_over_fused": round(r["t_s"] / r["t_f"], 4),
             **r["clock"],
         }
+        # the fraction of the peak at the clock the timed launch itself ran at
+        # (its measurement build, traced before and after the timing)
+        sclk = 0.5 * (r["clock"]["sclk_mhz_before"] + r["clock"]["sclk_mhz_after"])
+        if sclk > 0:
+            out["pct_bf16_peak_at_traced_clock"] = round(100 * r["value"] / (PEAK_BF16_TFLOPS * sclk / 2400.0), 2)
         if "unsplit" in r["cmp"]:
             out["unsplit_fused_ms_median"] = round(float(np.median(r["cmp"]["unsplit"])), 4)
         return out

@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.ua_epilogue_store_only.restype = i
     L.ua_work_units.argtypes = [sp, i]
     L.ua_work_units.restype = ctypes.c_int64
+    L.ua_work_units_ws.argtypes = [sp, i]
+    L.ua_work_units_ws.restype = ctypes.c_int64
+    L.attn_ulysses_fused_trace_ws.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp, ctypes.c_size_t, vp, vp]
+    L.attn_ulysses_fused_trace_ws.restype = i
     L.attn_ulysses_fused_io.argtypes = [vp, vp, vp, i, i, vp, sp, f, vp]
     L.attn_ulysses_fused_io.restype = i
     L.a2a_gather.argtypes = [vp, i, i, vp, sp, vp]
@@ -233,25 +237,36 @@ def a2a_gather(X, rank, P, X_local, stream=None):
         raise UAError("a2a_gather", st)
 
 
-def work_units(B, S, H, d, P) -> int:
-    return int(lib().ua_work_units(ctypes.byref(Shape(B, S, H, d)), int(P)))
+def work_units(B, S, H, d, P, workspace=False) -> int:
+    """Workgroups of the launch without (or, with workspace=True, with) a workspace."""
+    fn = lib().ua_work_units_ws if workspace else lib().ua_work_units
+    return int(fn(ctypes.byref(Shape(B, S, H, d)), int(P)))
 
 
-def attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None):
-    """Measurement build of attn_ulysses_fused; ``trace`` is an int64 GPU tensor
-    of work_units(...) * 4 elements (see the C header for its contents)."""
+def attn_ulysses_fused_trace(Q, K, V, rank, P, out, trace, scale=None, stream=None, workspace=None):
+    """Measurement build of attn_ulysses_fused (or, given a workspace, of
+    attn_ulysses_fused_ws); ``trace`` is an int64 GPU tensor of
+    work_units(..., workspace=...) * 4 elements (see the C header)."""
     import torch
     shp = _qkv_shape(Q, K, V, P)
     for n, t in (("Q", Q), ("K", K), ("V", V)):
         _check_bf16(n, t)
     _check_bf16("out", out, shp.B * shp.S * shp.H * shp.d)
-    n_units = int(lib().ua_work_units(ctypes.byref(shp), int(P)))
+    fn = lib().ua_work_units_ws if workspace is not None else lib().ua_work_units
+    n_units = int(fn(ctypes.byref(shp), int(P)))
     if trace.dtype != torch.int64 or not trace.is_cuda or not trace.is_contiguous() \
             or trace.numel() != 4 * n_units:
         raise TypeError("trace must be a contiguous int64 GPU tensor of %d elements" % (4 * n_units))
     scale = 1.0 / math.sqrt(shp.d) if scale is None else float(scale)
-    st = lib().attn_ulysses_fused_trace(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
-                                        ctypes.byref(shp), scale, _stream(stream, Q, K, V, out, trace), _ptr(trace))
+    if workspace is None:
+        st = lib().attn_ulysses_fused_trace(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
+                                            ctypes.byref(shp), scale, _stream(stream, Q, K, V, out, trace),
+                                            _ptr(trace))
+    else:
+        wp, wb = _ws(workspace)
+        st = lib().attn_ulysses_fused_trace_ws(_ptr(Q), _ptr(K), _ptr(V), int(rank), int(P), _ptr(out),
+                                               ctypes.byref(shp), scale, wp, wb,
+                                               _stream(stream, Q, K, V, out, trace, workspace), _ptr(trace))
     if st != UA_OK:
         raise UAError("attn_ulysses_fused_trace", st)
 

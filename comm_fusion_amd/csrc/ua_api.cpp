@@ -254,6 +254,14 @@ int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int ra
     return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, trace, true);
 }
 
+int attn_ulysses_fused_trace_ws(const void *Q, const void *K, const void *V, int rank, int P, void *out,
+                                const ua_shape *shp, float scale, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream, uint64_t *trace)
+{
+    return attention_call(Q, K, V, rank, P, out, shp, scale, stream, true, trace, true, false, true, workspace,
+                          workspace_bytes);
+}
+
 int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, hipStream_t stream)
 {
     int64_t elems = 0;
@@ -274,6 +282,14 @@ int64_t ua_work_units(const ua_shape *shp, int P)
     if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
     if (empty(shp)) return 0;
     return ua::attention_units(shp->B, shp->S, shp->H / P, (int)shp->d);
+}
+
+int64_t ua_work_units_ws(const ua_shape *shp, int P)
+{
+    int64_t elems = 0;
+    if (check_shape(shp, 0, P, &elems) != UA_OK || check_limits(shp, P) != UA_OK) return 0;
+    if (empty(shp)) return 0;
+    return ua::attention_units_ws(shp->B, shp->S, shp->H / P, (int)shp->d);
 }
 
 int a2a_permute(const void *O_local, int rank, int P, void *out, const ua_shape *shp, hipStream_t stream)

@@ -69,6 +69,9 @@ int device_xcd_count();
 // Work units (one workgroup each) the attention launch uses for this shape
 // without a key split (query tiles).
 int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d);
+// Workgroups of the launch given a workspace (the key split's, or the plain
+// launch's when it does not split).
+int64_t attention_units_ws(int64_t B, int64_t S, int64_t Hl, int d);
 
 // Workgroups per query tile of a launch given a workspace (1: no split), and
 // the workspace bytes that launch needs (0 when it does not split).

@@ -223,15 +223,16 @@ __device__ __forceinline__ int xcd_unit(int bid, int n, int nx)
 // all of them in split order -- the same arithmetic whichever workgroup
 // arrives last -- and stores the rows like the unsplit kernel.
 // TRACE: measurement build with the same arithmetic and output, which also
-// records per work unit (in a.trace[4*unit ..]): the 100 MHz constant clock
-// at the start, when every wave has its normalised rows ready (a workgroup
-// barrier), when every wave's epilogue stores have completed (vmcnt(0) and a
-// barrier), and the shader-clock cycles from start to end.
+// records per workgroup (in a.trace[4*u ..], u its work unit, or its run of
+// a key-split launch): the 100 MHz constant clock at the start, when every
+// wave last had its normalised rows ready (a workgroup barrier; the end,
+// if it stored no rows), at the end once every wave's stores have completed
+// (vmcnt(0) and a barrier), and the shader-clock cycles from start to end.
 template <int D, int NW, int RB, int KB, int KS, bool XS, bool TRACE>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void attn_fwd(AttnArgs a)
 {
-    uint64_t tr_t0 = 0, tr_c0 = 0;
+    uint64_t tr_t0 = 0, tr_c0 = 0, tr_rows = 0;
     if constexpr (TRACE) {
         tr_t0 = __builtin_amdgcn_s_memrealtime();
         tr_c0 = __builtin_amdgcn_s_memtime();
@@ -1013,19 +1014,7 @@ void attn_fwd(AttnArgs a)
             }
         }
     }
-    if constexpr (TRACE) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const uint64_t tr_se = __builtin_amdgcn_s_memrealtime();
-        const uint64_t tr_c1 = __builtin_amdgcn_s_memtime();
-        if (threadIdx.x == 0) {
-            uint64_t *t = a.trace + 4 * (int64_t)unit;
-            t[0] = tr_t0;
-            t[1] = tr_sb;
-            t[2] = tr_se;
-            t[3] = tr_c1 - tr_c0;
-        }
-    }
+    if constexpr (TRACE) tr_rows = tr_sb;
     };
 
     // The work of this workgroup, one call site so the body is inlined once.
@@ -1088,6 +1077,19 @@ void attn_fwd(AttnArgs a)
         }
         run(wid, qt, bh, kt0, ntl, part, nparts);
     } while (sk && it < end);
+    if constexpr (TRACE) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const uint64_t tr_se = __builtin_amdgcn_s_memrealtime();
+        const uint64_t tr_c1 = __builtin_amdgcn_s_memtime();
+        if (threadIdx.x == 0) {
+            uint64_t *t = a.trace + 4 * (int64_t)wid;
+            t[0] = tr_t0;
+            t[1] = tr_rows ? tr_rows : tr_se;
+            t[2] = tr_se;
+            t[3] = tr_c1 - tr_c0;
+        }
+    }
 }
 
 // Epilogue stores alone: the attention kernel's grid, work-unit order and
@@ -1426,14 +1428,15 @@ const void *attention_kernel(int d, const LaunchShape &ls)
 }
 
 // The key-split builds (8-wave shapes only).
+template <bool TRACE>
 const void *attention_kernel_xs(int d, const LaunchShape &ls)
 {
     if (d == 128)
-        return ls.ks == 2 ? (const void *)attn_fwd<128, 8, 1, 32, 2, true, false>
-                          : (const void *)attn_fwd<128, 8, 1, 64, 1, true, false>;
-    if (ls.ks == 2) return (const void *)attn_fwd<64, 8, 1, 32, 2, true, false>;
-    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, 1, true, false>;
-    return (const void *)attn_fwd<64, 8, 1, 64, 1, true, false>;
+        return ls.ks == 2 ? (const void *)attn_fwd<128, 8, 1, 32, 2, true, TRACE>
+                          : (const void *)attn_fwd<128, 8, 1, 64, 1, true, TRACE>;
+    if (ls.ks == 2) return (const void *)attn_fwd<64, 8, 1, 32, 2, true, TRACE>;
+    if (ls.rb == 2) return (const void *)attn_fwd<64, 8, 2, 32, 1, true, TRACE>;
+    return (const void *)attn_fwd<64, 8, 1, 64, 1, true, TRACE>;
 }
 
 // Workspace of a key-split launch: one uint32 arrival count per query tile
@@ -1456,6 +1459,15 @@ int64_t attention_units(int64_t B, int64_t S, int64_t Hl, int d)
 {
     const LaunchShape ls = launch_shape(B, S, Hl, d, device_info().cus);
     return B * Hl * ((S + ls.rows() - 1) / ls.rows());
+}
+
+int64_t attention_units_ws(int64_t B, int64_t S, int64_t Hl, int d)
+{
+    const SplitPlan sp = split_plan(B, S, Hl, d, device_info().cus);
+    const int64_t units = B * Hl * ((S + sp.ls.rows() - 1) / sp.ls.rows());
+    if (sp.n <= 1) return attention_units(B, S, Hl, d);
+    if (sp.sk_iters > 0) return (units * ((S + sp.ls.kb - 1) / sp.ls.kb) + sp.sk_iters - 1) / sp.sk_iters;
+    return units * sp.n;
 }
 
 int key_split(int64_t B, int64_t S, int64_t Hl, int d) { return split_plan(B, S, Hl, d, device_info().cus).n; }
@@ -1485,8 +1497,8 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
                             uint64_t *trace, void *workspace, unsigned *wcount)
 {
     const DeviceInfo dv = device_info();
-    const SplitPlan sp = workspace && !trace ? split_plan(B, S, Hl, d, dv.cus)
-                                             : SplitPlan{launch_shape(B, S, Hl, d, dv.cus), 1, 0};
+    const SplitPlan sp = workspace ? split_plan(B, S, Hl, d, dv.cus)
+                                   : SplitPlan{launch_shape(B, S, Hl, d, dv.cus), 1, 0};
     const LaunchShape ls = sp.ls;
     const int n_split = sp.n;
     AttnArgs a;
@@ -1517,7 +1529,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, const uint16_t
         // per CU; the last run may be shorter); else n_split per query tile
         const int64_t total = (int64_t)a.n_units * ((S + ls.kb - 1) / ls.kb);
         a.n_units = sp.sk_iters > 0 ? (int32_t)((total + sp.sk_iters - 1) / sp.sk_iters) : a.n_units * n_split;
-        fn = attention_kernel_xs(d, ls);
+        fn = trace ? attention_kernel_xs<true>(d, ls) : attention_kernel_xs<false>(d, ls);
     } else {
         fn = trace ? attention_kernel<true>(d, ls) : attention_kernel<false>(d, ls);
     }

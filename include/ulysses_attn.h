@@ -244,6 +244,21 @@ int attn_ulysses_fused_trace(const void *Q, const void *K, const void *V, int ra
                              uint64_t *trace);
 
 /*
+ * The measurement build of attn_ulysses_fused_ws: the same launch (the key
+ * split or stream-K runs where the shape splits) and bit-identical output,
+ * with one trace record per workgroup, trace[4*u + 0..3], u in
+ * [0, ua_work_units_ws): [0] the 100 MHz clock at its start, [1] when its
+ * waves last had normalised rows ready to store ([2] if it stored none: a
+ * part of a split query tile that another workgroup merged), [2] once its
+ * stores have completed, at its end, [3] shader-clock cycles from [0] to
+ * [2].  So a split launch's clock is read on the launch itself.  Workspace
+ * as attn_ulysses_fused_ws; trace as attn_ulysses_fused_trace.
+ */
+int attn_ulysses_fused_trace_ws(const void *Q, const void *K, const void *V, int rank, int P,
+                                void *out, const ua_shape *shp, float scale, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream, uint64_t *trace);
+
+/*
  * Write check of the fused path ("every destination element is written
  * exactly once"): attn_ulysses_fused_ws (the key split, stream-K, or the
  * plain call where the shape needs no workspace) that also adds 1 to
@@ -272,6 +287,11 @@ int ua_epilogue_store_only(int rank, int P, void *out, const ua_shape *shp, hipS
  * per unit); 0 for an invalid or empty shape.  A *_ws call that splits runs
  * ua_key_split workgroups per query tile of its own launch shape. */
 int64_t ua_work_units(const ua_shape *shp, int P);
+
+/* Workgroups of the launch of a *_ws call (the key split's or stream-K
+ * runs when it splits, else ua_work_units), and so the records of
+ * attn_ulysses_fused_trace_ws; 0 for an invalid or empty shape. */
+int64_t ua_work_units_ws(const ua_shape *shp, int P);
 
 /* Static English text for a status code; never NULL. */
 const char *ua_status_string(int status);

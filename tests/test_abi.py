@@ -307,6 +307,36 @@ def test_write_counts_validates_its_counter_buffer():
     assert call((1, 16384, 40, 128), ws=A + 8192, ws_bytes=64) == ua.UA_ERR_WORKSPACE
 
 
+def test_traced_workspace_call_validates_and_counts_its_workgroups():
+    L = ua.lib()
+    L.attn_ulysses_fused_trace_ws.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_void_p, ctypes.c_float,
+                                                                       ctypes.c_void_p, ctypes.c_size_t,
+                                                                       ctypes.c_void_p, ctypes.c_void_p]
+
+    def call(shape=(1, 16384, 40, 128), rank=0, P=8, trace=O + 4096, out=O, ws=A + 8192, ws_bytes=1 << 30):
+        return L.attn_ulysses_fused_trace_ws(A, B_, C, rank, P, out, ctypes.byref(Shape(*shape)), 0.125,
+                                             ws, ws_bytes, None, trace)
+
+    assert call(trace=0) == ua.UA_ERR_NULL
+    assert call(trace=O + 4100) == ua.UA_ERR_ALIGN
+    assert call(ws=0) == ua.UA_ERR_NULL                 # this shape splits: it needs the workspace
+    assert call(ws_bytes=64) == ua.UA_ERR_WORKSPACE
+    # workgroups of the split launch: the stream-K runs (one per CU), more
+    # than the query tiles of the plain launch; equal otherwise
+    for shape in ((1, 16384, 24, 128), (1, 16384, 40, 128), (1, 4096, 24, 128)):
+        plain, split = ua.work_units(*shape, 8), ua.work_units(*shape, 8, workspace=True)
+        if ua.key_split(*shape, 8) > 1:
+            if ua.stream_k_iters(*shape, 8):
+                B, S, H, d = shape
+                total = plain * -(-S // 64)
+                assert split == -(-total // ua.stream_k_iters(*shape, 8))
+            else:
+                assert split == plain * ua.key_split(*shape, 8)
+        else:
+            assert split == plain
+    assert ua.work_units(1, 512, 4, 64, 2, workspace=True) == ua.work_units(1, 512, 4, 64, 2)
+
+
 def test_tile_override_from_the_environment():
     """UA_TILE forces the launch shape (read once per process, so each
     setting runs in a fresh interpreter); unknown values and shapes it does
