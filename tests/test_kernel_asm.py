@@ -501,3 +501,75 @@ def test_persistent_moe_reads_act_at_device_scope():
     assert not [l for l in lds_copies.findall(tiles) if re.search(r"\bsc1\b", l)]
     # thread 0's acquire after it observes the count (pairs with the release)
     assert re.search(r"^\s*buffer_inv sc1\b", persist, re.M)
+
+
+# ---- d = 64: the issue priority is raised only for a slot's softmax slice ----
+#
+# At d = 64 each steady-loop slot raises the wave's issue priority
+# (s_setprio 1) for its VALU slice and drops it (s_setprio 0) before the next
+# slot's MFMA.  Check over the control-flow graph that no s_barrier,
+# s_endpgm or MFMA is reached while the priority may still be raised, and
+# that only the d = 64 kernels change it.
+
+_PRIO = re.compile(r"^s_setprio\s+(\S+)")
+
+
+def _prio_step(raised: bool, line: str, bad, i):
+    m = _PRIO.match(line)
+    if m:
+        return int(m.group(1), 0) != 0
+    if raised and bad is not None and line.startswith(("s_barrier", "s_endpgm", "v_mfma")):
+        bad.append((i, line))
+    return raised
+
+
+def raised_priority_reaches(lines):
+    """Barriers, program ends and MFMAs reachable with the priority raised."""
+    blocks, succ = _blocks(lines)
+    inn = [None] * len(blocks)
+    inn[0] = False
+    work = [0]
+    while work:
+        k = work.pop()
+        st = inn[k]
+        for i, line in blocks[k]:
+            st = _prio_step(st, line, None, i)
+        for t in succ[k]:
+            m = st if inn[t] is None else (inn[t] or st)
+            if m != inn[t]:
+                inn[t] = m
+                work.append(t)
+    bad = []
+    for k, blk in enumerate(blocks):
+        st = bool(inn[k])
+        for i, line in blk:
+            st = _prio_step(st, line, bad, i)
+    return bad
+
+
+def test_d64_priority_covers_only_the_softmax_slices(asm):
+    bodies = _kernel_bodies(asm)
+    d64 = {n: l for n, l in bodies.items() if "attn_fwdILi64E" in n}
+    d128 = {n: l for n, l in bodies.items() if "attn_fwdILi128E" in n}
+    assert d64 and d128
+    for name, lines in d64.items():
+        raises = [l for l in lines if _PRIO.match(l) and int(_PRIO.match(l).group(1), 0) != 0]
+        # one raise per steady-loop slot: as many as the loop has MFMAs, at least
+        assert len(raises) >= 16, name
+        bad = raised_priority_reaches(lines)
+        assert not bad, "%s: %s" % (name, bad[:3])
+    for name, lines in d128.items():
+        assert not [l for l in lines if _PRIO.match(l)], name
+
+
+def test_priority_checker_catches_a_raise_held_into_a_barrier():
+    ok = ["s_setprio 1", "v_exp_f32_e32 v1, v1", "s_setprio 0",
+          "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", "s_barrier", "s_endpgm"]
+    assert raised_priority_reaches(ok) == []
+    # the drop sits on one path only: the other reaches the barrier raised
+    bad = ["s_setprio 1", "v_exp_f32_e32 v1, v1", "s_cbranch_scc1 .LBB0_2",
+           "s_setprio 0", ".LBB0_2:", "s_barrier", "s_endpgm"]
+    assert raised_priority_reaches(bad) == [(5, "s_barrier"), (6, "s_endpgm")]
+    # an MFMA issued before the drop
+    late = ["s_setprio 1", "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]", "s_setprio 0"]
+    assert raised_priority_reaches(late) == [(1, late[1])]
