@@ -30,8 +30,10 @@
  *       [B][S][H][d] tensor: running every rank fills the full output.)
  *
  * Ownership: the caller allocates and frees every buffer (the *_ws calls'
- * workspace included); the library allocates nothing and keeps no state
- * between calls.  A call writes only
+ * workspace included); the library allocates nothing.  Between calls it
+ * keeps only the device facts it queries once per device (compute units,
+ * XCDs) and, for attn_ulysses_fused_noalloc, that call's fixed device
+ * scratch (a static array, held until the process ends).  A call writes only
  * this rank's Hl head slots of `out` (every other slot keeps its bytes).
  * Output buffers must not overlap the inputs.
  *
@@ -128,8 +130,9 @@ int a2a_permute(const void *O_local, int rank, int P, void *out,
 
 /*
  * The fused and serial calls with a workspace, for shapes whose query tiles
- * leave CUs idle: fewer tiles than the GPU's 256 CUs (short sequences, few
- * local heads), or a last round over the CUs that few tiles fill.  The
+ * leave CUs idle: fewer tiles than the GPU has compute units (256 on an
+ * MI355X; short sequences, few local heads), or a last round over the CUs
+ * that few tiles fill.  The
  * computation is the same (Fig. 6 of the review page: each output tile has
  * one owner, which stores it into its destination slot, Fig. 7), except that
  * the keys of each query tile are split over ua_key_split workgroups: each
