@@ -303,7 +303,7 @@ def traced_call(ua, torch, q, k, v, w, dest, workspace=None) -> dict:
 
 
 LONG_CONFIGS = ("video_dit", "dit_long", "mixed")   # the long-sequence workloads the target covers
-WARM_MS = 200.0          # launches run for at least this long before any timing
+WARM_MS = 1000.0         # launches run for at least this long before any timing
 DVFS_BAND = 0.02         # the pages' +-2% clock envelope (Fig. 11 caption)
 
 
