@@ -282,12 +282,21 @@ def traced_call(ua, torch, q, k, v, w, dest, workspace=None) -> dict:
     trace = torch.zeros(4 * n, dtype=torch.int64, device=q.device)
     ua.attn_ulysses_fused_trace(q, k, v, w.rank, w.P, dest, trace, workspace=workspace)
     torch.cuda.synchronize()
-    t = trace.cpu().numpy().reshape(n, 4).astype(np.float64)
+    return trace_stats(trace.cpu().numpy().reshape(n, 4), w.out_bytes)
+
+
+def trace_stats(records, out_bytes) -> dict:
+    """Statistics of a measurement build's records, one row per workgroup:
+    [start, rows ready, stores complete] on the 100 MHz constant clock, then
+    shader cycles from start to stores complete.  out_bytes: the bytes the
+    launch's epilogues store in all."""
+    t = np.asarray(records, dtype=np.float64)
+    n = len(t)
     # a split launch's parts merged elsewhere store nothing: [1] == [2]
     span_us = (t[:, 2] - t[:, 1]) / 100.0          # 100 MHz ticks -> us
     life_us = (t[:, 2] - t[:, 0]) / 100.0
     ok = span_us > 0                                # the workgroups that stored rows
-    unit_bytes = w.out_bytes / max(int(ok.sum()), 1)  # mean bytes a storing workgroup stores
+    unit_bytes = out_bytes / max(int(ok.sum()), 1)  # mean bytes a storing workgroup stores
     unit_mhz = t[:, 3] / np.maximum(life_us, 1e-3)   # cycles per us = MHz
     sp = span_us[ok] if ok.any() else span_us
     return {
