@@ -109,6 +109,51 @@ def test_key_split_call_replays_from_a_graph():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
+def test_noalloc_call_replays_from_a_graph():
+    # The call for callers that cannot allocate: its key-split workspace is
+    # the library's fixed scratch, whose arrival counts each call clears with
+    # a small kernel (no memset), so it can be captured.  Between replays an
+    # eager call of another split shape leaves its own partials and counts
+    # in the scratch; every replay must still return the eager call's bits.
+    import torch
+    B, S, H, P, rank, d = 1, 4096, 24, 8, 3, 128
+    assert ua.key_split(B, S, H, d, P) > 1
+    q, k, v = (to_dev(x).view(B, S, H // P, d) for x in make_qkv(B, S, H // P, d, 33))
+    out = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused_noalloc(q, k, v, rank, P, out)   # first call on the device: set-up, eager
+    torch.cuda.synchronize()
+    ref = out.clone()
+    ws = ua.new_workspace(B, S, H, d, P, q.device)
+    via_ws = sentinel_buffer(B * S * H * d)
+    ua.attn_ulysses_fused_ws(q, k, v, rank, P, via_ws, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), via_ws.view(torch.int16))
+    # another split shape for the eager calls between replays (d = 64, two row blocks)
+    B2, S2, H2, P2, r2, d2 = 1, 16384, 48, 8, 1, 64
+    assert ua.key_split(B2, S2, H2, d2, P2) > 1
+    q2, k2, v2 = (to_dev(x).view(B2, S2, H2 // P2, d2) for x in make_qkv(B2, S2, H2 // P2, d2, 34))
+    out2 = sentinel_buffer(B2 * S2 * H2 * d2)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ua.attn_ulysses_fused_noalloc(q, k, v, rank, P, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ua.attn_ulysses_fused_noalloc(q, k, v, rank, P, out)
+    sentinel = SENTINEL_BITS - 0x10000 if SENTINEL_BITS >= 0x8000 else SENTINEL_BITS
+    for _ in range(3):
+        ua.attn_ulysses_fused_noalloc(q2, k2, v2, r2, P2, out2)
+        out.view(torch.int16).fill_(sentinel)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
 def test_moe_experts_combine_replays_from_a_graph():
     """The MoE path (several launches per call, both schedules, and the
     persistent form with its workspace clear) inside a graph: every replay
