@@ -35,14 +35,24 @@
 //  * software pipeline: in steady state, iteration t interleaves the
 //    softmax of S_t with the MFMAs of O += V_{t-1} P_{t-1} and of S_{t+1},
 //    one MFMA plus a slice of softmax VALU work per issue slot, so every
-//    wave keeps its matrix pipe fed while it does its exponentials;
+//    wave keeps its matrix pipe fed while it does its exponentials (at
+//    d = 64, where every slot carries VALU work, each slice issues at raised
+//    wave priority);
 //  * online softmax in fp32, log2 domain, with a lazily raised running max:
 //    the tiles between a work item's first and last take P against the max
 //    as it stands (no tile max in the loop) and go to an exact path only
 //    when a lane's sum of the tile's P passes 2^15;
-//  * epilogue: each lane normalises its row and stores it straight to the
-//    destination slot computed from (rank, P) -- the fused All-to-All.  The
-//    local (serial) output is the same epilogue with one region;
+//  * epilogue: each wave normalises its rows, stages them through the LDS
+//    (free after the loop) and stores whole rows, 16 bytes per lane, straight
+//    into the destination slots computed from (rank, P) -- the fused
+//    All-to-All.  The local (serial) output is the same epilogue with one
+//    region;
+//  * launches whose query tiles leave CUs idle (the calls with a workspace)
+//    split each tile's keys over several workgroups, in equal runs or
+//    stream-K (equal runs of (query tile, key tile) iterations across tile
+//    boundaries); the parts write their partial softmax state to the
+//    workspace at device scope and the last to arrive merges them in key
+//    order and stores the tile;
 //  * workgroup ids are remapped so that consecutive work units of one head
 //    run on the same XCD and share its L2 while they stream the same K/V;
 //  * Q, K, V rows are read with a row stride of in_heads*d: the local layout
