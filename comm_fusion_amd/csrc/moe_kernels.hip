@@ -32,7 +32,14 @@
 //    dispatch exchange's receive side is read in place;
 //  * the Linear-2 epilogue multiplies each row by its routing weight, rounds
 //    to bf16, stages the tile in the LDS and stores whole 512-byte row
-//    segments (16 bytes per lane) into each row's Combine slot.
+//    segments (16 bytes per lane) into each row's Combine slot;
+//  * a wave skips the MFMAs and operand reads of its 32-row token blocks
+//    that lie past its expert's last row (a partial tile still copies its
+//    weight slice and meets every barrier);
+//  * the persistent form runs a whole schedule in one launch: workgroups
+//    take tiles in schedule order from a device queue, and a Linear-2 tile
+//    first waits (bounded) until the Linear-1 tiles of its token rows have
+//    counted themselves done (moe_persist, below).
 #include "moe_internal.h"
 #include "ua_internal.h"
 
