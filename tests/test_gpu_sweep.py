@@ -8,8 +8,12 @@ the exact destination layout, and for bit equality between the fused call,
 the serial attention + permute, and the fused call on sequence-partitioned
 inputs.  A third sweep does the same for the calls with a workspace on shapes
 whose query tiles are few enough for a key split.
+
+UA_SWEEP_WIDE=1 in the environment swaps in wider draws from other seeds
+(150 + 60 shapes for the plain calls, 60 for the key split) for a longer run.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -44,7 +48,8 @@ def sweep_shapes(n=32, seed=2026):
     return out
 
 
-SHAPES = sweep_shapes()
+WIDE = os.environ.get("UA_SWEEP_WIDE") == "1"
+SHAPES = sweep_shapes(150, 9101) if WIDE else sweep_shapes()
 
 
 def sweep_shapes_b(n=16, seed=2027):
@@ -76,7 +81,7 @@ def sweep_shapes_b(n=16, seed=2027):
     return out
 
 
-SHAPES_B = sweep_shapes_b()
+SHAPES_B = sweep_shapes_b(60, 9102) if WIDE else sweep_shapes_b()
 
 
 def sweep_shapes_split(n=12, seed=2028):
@@ -97,7 +102,7 @@ def sweep_shapes_split(n=12, seed=2028):
     return out
 
 
-SHAPES_SPLIT = sweep_shapes_split()
+SHAPES_SPLIT = sweep_shapes_split(60, 9103) if WIDE else sweep_shapes_split()
 
 
 def _dev(a):
