@@ -9,8 +9,11 @@ come up).  Each shape is checked against the fp64 oracle on every served
 Combine slot with the layout exact (test_gpu_moe's tolerance), and the other
 forms must write the same bytes: the other schedule, another wave size, the
 persistent form (one launch, device tile queue) and the serial form
-(experts, then the scatter).
+(experts, then the scatter).  UA_SWEEP_WIDE=1 in the environment draws 80
+shapes from another seed instead.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -41,7 +44,7 @@ def moe_sweep_shapes(n=16, seed=2029):
     return out
 
 
-SHAPES = moe_sweep_shapes()
+SHAPES = moe_sweep_shapes(80, 9104) if os.environ.get("UA_SWEEP_WIDE") == "1" else moe_sweep_shapes()
 
 
 @pytest.mark.parametrize("w", SHAPES, ids=[s.name for s in SHAPES])
