@@ -10,6 +10,8 @@ checker) the oracle on sampled rows, the layout, attn_serial_ws +
 a2a_permute writing exactly the fused bytes, a second call on the same
 workspace bit-equal, and the arrival counts back at zero.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -35,3 +37,34 @@ def test_stream_k_matches_oracle_and_serial(B, S, H, P, rank, d, seed):
     Q, K, V = make_qkv(B, S, H // P, d, seed)
     w = Workload("t", B, S, H, P, rank, d, seed, sampled=True)
     _check_split_call(Q, K, V, H, P, rank, sampled_rows(w, n_per_head=64), "stream-K %s" % ((B, S, H, d),))
+
+
+def stream_k_sweep_shapes(n=12, seed=2030):
+    """Random valid shapes on which the plan picks stream-K (the choice is a
+    host computation for the full MI355X): B 1-2, P in {1, 2, 4, 8} and any
+    rank, 1-8 local heads, both head dims, 2000-20000 keys, mostly ragged;
+    at most 3e7 elements per input."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        d = int(rng.choice([64, 128]))
+        P = int(rng.choice([1, 2, 4, 8]))
+        Hl = int(rng.integers(1, 9))
+        B = int(rng.integers(1, 3))
+        S = P * int(rng.integers(max(1, 2000 // P), 1 + 20000 // P))
+        if B * S * Hl * d > 3e7 or ua.stream_k_iters(B, S, Hl * P, d, P) <= 0:
+            continue
+        out.append((B, S, Hl * P, P, int(rng.integers(0, P)), d, 800 + len(out)))
+    return out
+
+
+SWEEP = stream_k_sweep_shapes(48, 9105) if os.environ.get("UA_SWEEP_WIDE") == "1" else stream_k_sweep_shapes()
+
+
+@pytest.mark.parametrize("B,S,H,P,rank,d,seed", SWEEP)
+def test_stream_k_sweep(B, S, H, P, rank, d, seed):
+    # UA_SWEEP_WIDE=1 draws 48 shapes from another seed instead of 12
+    print("stream-K sweep case", (B, S, H, P, rank, d, seed), flush=True)
+    Q, K, V = make_qkv(B, S, H // P, d, seed)
+    w = Workload("t", B, S, H, P, rank, d, seed, sampled=True)
+    _check_split_call(Q, K, V, H, P, rank, sampled_rows(w, n_per_head=32), "stream-K sweep %s" % ((B, S, H, d),))
