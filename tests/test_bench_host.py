@@ -1,7 +1,7 @@
 """Host-side logic of bench.py (CPU only): the kernel code digest that ties
 the committed counter figures to the code they were taken on, the statistics
 of the measurement build's per-workgroup records (store spans, shader clock),
-and the +-2% DVFS flag on a timing."""
+the +-2% DVFS flag on a timing, and the refusal of more than one GPU."""
 import bench
 
 
@@ -71,3 +71,11 @@ def test_clock_flags_mark_drift_and_spread_beyond_two_percent():
     assert f["launch_spread_pct"] == 4.76 and f["outside_dvfs_band"]
     # a clock that could not be read counts as outside
     assert bench.clock_flags(0.0, 0.0, steady)["outside_dvfs_band"]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
